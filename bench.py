@@ -1,0 +1,195 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME]
+
+A step is one moe_forward call (router GEMM, top-k, dispatch, grouped-GEMM
+experts + shared expert, combine) over one batch of seeded synthetic tokens
+resident in HBM. Prints one JSON line with tokens/s, the roofline of the
+dominant kernel (measured with HIP events over the timed steps) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at 1 GPU; grouped-GEMM % MFMA peak / % HBM GB/s"
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0        # dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_F32_TFLOPS = 157.3          # fp32 MFMA/vector
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="ep8_decode_bf16")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--cpu-sample", type=int, default=64, help="tokens of the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def stage_bytes_flops(w, counts, stage):
+    """Algorithmic HBM bytes and FLOPs of one launch of `stage`.
+
+    GroupGEMM I/O model g*(m*k + n*k + m*n) elements and 2*g*m*k*n FLOPs
+    (Perplexity, "Roofline > GroupGEMM"), with m_i the rows of expert i, only
+    experts with rows counted, each term at its stored element size."""
+    H, I, Is, T = w["hidden"], w["inter"], w["shared_inter"], w["T"]
+    eb = {"bf16": 2, "f32": 4, "fp8": 1}[w["dtype"]]
+    R = int(counts.sum())
+    active = int((counts > 0).sum())
+    if stage == "gate_up":
+        return (R * H + active * 2 * I * H + R * I) * eb, 2.0 * R * H * 2 * I
+    if stage == "down":
+        return (R * I + active * H * I) * eb + R * H * max(eb, 2), 2.0 * R * I * H
+    if stage == "shared_gate_up":
+        return (T * H + 2 * Is * H + T * Is) * eb, 2.0 * T * H * 2 * Is
+    if stage == "shared_down":
+        return (T * Is + H * Is) * eb + T * H * max(eb, 2), 2.0 * T * Is * H
+    raise ValueError(stage)
+
+
+def cpu_baseline(w, inp, sample):
+    """The oracle as it stands, timed on the first `sample` tokens."""
+    import platform
+    from oracle import moe_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+
+    def h(t):
+        if t is None:
+            return None
+        t = t.detach().cpu()
+        return t.float().numpy() if t.dtype.is_floating_point and t.dtype != __import__("torch").float8_e4m3fn \
+            else t.view(__import__("torch").uint8).numpy()
+
+    cfg = O.Config.from_workload(w)
+    S = min(sample, w["T"])
+    x = h(inp["x"][:S])
+    args = dict(router_bias=h(inp["router_bias"]), score_bias=h(inp["score_bias"]),
+                shared_w13=h(inp["shared_w13"]), shared_w2=h(inp["shared_w2"]))
+    scales = {k: h(inp.get(k)) for k in ("w13_scale", "w2_scale", "shared_w13_scale", "shared_w2_scale")}
+    wr, w13, w2 = h(inp["w_router"]), h(inp["w13"]), h(inp["w2"])
+    t0 = time.perf_counter()
+    O.forward(cfg, x, wr, w13, w2, scales=scales, **args)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": S / dt, "unit": "tokens/s", "cores": blas_threads or cores, "kind": "oracle",
+            "sample": f"first {S} of {w['T']} tokens of the same workload, whole layer "
+                      f"(route, dispatch, experts, shared expert, combine), {dt:.1f} s wall",
+            "affinity_cores": cores, "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU: --gpus {a.gpus} is not supported by this build "
+              "(the layer runs one GPU's share of experts; no collectives).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mixture_experts_layer_10_amd as moe
+    from synth import make_inputs, workload
+
+    w = workload(a.config)
+    T = w["T"]
+    print(f"[bench] config {a.config}: T={T} H={w['hidden']} E={w['n_experts']} "
+          f"local=[{w['expert_begin']},{w['expert_end']}) dtype={w['dtype']}", file=sys.stderr, flush=True)
+    inp = make_inputs(w, device="cuda")
+    cfg = moe.config_from_workload(w, out_dtype=a.out_dtype)
+    W = moe.make_weights(cfg, inp["w13"], inp["w2"], inp["shared_w13"], inp["shared_w2"], inp.get("w13_scale"),
+                         inp.get("w2_scale"), inp.get("shared_w13_scale"), inp.get("shared_w2_scale"))
+    ws = moe.workspace(cfg, T)
+    y = torch.empty(T, w["hidden"], dtype=torch.bfloat16 if a.out_dtype == "bf16" else torch.float32,
+                    device="cuda")
+    ids = torch.empty(T, w["top_k"], dtype=torch.int32, device="cuda")
+
+    def step():
+        moe.moe_forward(cfg, inp["x"], inp["w_router"], inp["router_bias"], inp["score_bias"], W, y, ws,
+                        topk_ids_out=ids)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.profile_enable(a.steps * len(moe.STAGES) + 16)
+    moe.profile_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = moe.profile_query()
+    moe.profile_enable(0)
+    ms = (t1 - t0) * 1e3 / a.steps
+    value = T / (ms * 1e-3)
+
+    ids_h = ids.cpu().numpy().reshape(-1)
+    loc = ids_h[(ids_h >= w["expert_begin"]) & (ids_h < w["expert_end"])] - w["expert_begin"]
+    counts = np.bincount(loc, minlength=w["expert_end"] - w["expert_begin"])
+    if w["capacity_factor"] > 0:
+        import math
+        cap = math.ceil(float(np.float32(w["capacity_factor"])) * T * w["top_k"] / w["n_experts"])
+        counts = np.minimum(counts, cap)
+
+    stage_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in prof.items()}
+    gemm_stages = [s for s in ("gate_up", "down", "shared_gate_up", "shared_down") if stage_ms[s] > 0]
+    dom = max(gemm_stages, key=lambda s: stage_ms[s])
+    byts, flops = stage_bytes_flops(w, counts, dom)
+    t_dom = stage_ms[dom] * 1e-3
+    peak_mfma = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "f32": PEAK_F32_TFLOPS}[w["dtype"]]
+    ridge = peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / byts < ridge:
+        roof = {"bound": "hbm", "achieved": byts / t_dom / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": peak_mfma, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = f"gemm_kernel ({dom})"
+    roof["kernel_ms"] = stage_ms[dom]
+    roof["algorithmic_bytes"] = byts
+    roof["algorithmic_flops"] = flops
+
+    # grouped GEMM as a whole (routed gate/up + down): both roofline fractions
+    gb, gf = 0.0, 0.0
+    for s in ("gate_up", "down"):
+        b_, f_ = stage_bytes_flops(w, counts, s)
+        gb += b_
+        gf += f_
+    gt = (stage_ms["gate_up"] + stage_ms["down"]) * 1e-3
+    grouped = {"ms": gt * 1e3, "hbm_frac": gb / gt / 1e9 / PEAK_HBM_GBS,
+               "mfma_frac": gf / gt / 1e12 / peak_mfma}
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic",
+        "config": {"workload": a.config, "tokens": T, "hidden": w["hidden"], "experts": w["n_experts"],
+                   "local_experts": [w["expert_begin"], w["expert_end"]], "top_k": w["top_k"],
+                   "inter": w["inter"], "shared_inter": w["shared_inter"], "out_dtype": a.out_dtype},
+        "roofline": roof,
+        "grouped_gemm": grouped,
+        "stage_ms": stage_ms,
+        "rows": int(counts.sum()), "max_rows_per_expert": int(counts.max()),
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

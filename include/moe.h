@@ -1,0 +1,227 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) MoE layer forward library, libmoe.so.
+ *
+ * The layer is the DeepSeek-V3/R1-style mixture-of-experts FFN:
+ *   route    -> a router GEMM gives per-expert logits; scores, group-limited
+ *               top-k and gates pick k experts per token;
+ *   dispatch -> tokens are permuted into expert-contiguous order;
+ *   experts  -> each local expert runs a SwiGLU FFN on its rows (a grouped
+ *               GEMM), plus the shared expert on every token;
+ *   combine  -> each token's k expert outputs are un-permuted, weighted by
+ *               the gates and summed, and the shared output is added.
+ * Sources: Ultralytics glossary "Expert Parallelism" (section "How tokens
+ * move between GPUs": route, dispatch, compute, combine; section "Load
+ * balancing and capacity": capacity factor, selection-only bias); Perplexity
+ * "Lower latency and higher throughput with multi-node DeepSeek deployment"
+ * (sections "Expert parallelism", "Roofline > GroupGEMM", "Quantization",
+ * "MoE Router"); NVIDIA "Optimizing DeepSeek R1 throughput on Blackwell"
+ * (section "MoE layer optimisations": mixed-precision router GEMM, fused
+ * group-limited top-k); infra guide "Data parallelism and expert parallelism"
+ * (section 2.1: shapes; section 3.1: the four steps).
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" are device memory owned by the caller; the
+ *    library never allocates or frees device memory and keeps no per-call
+ *    state. `ws` is a caller-owned device workspace of at least the size
+ *    moe_workspace_bytes() reports for the same config and token count.
+ *  - Every call is asynchronous and ordered on `stream`; outputs are valid
+ *    when the stream reaches that point. No call synchronises or reads
+ *    device data on the host, so calls can be captured in a HIP graph.
+ *  - Arguments are validated before anything is enqueued: a nonzero return
+ *    means nothing was launched. T == 0 is a successful no-op.
+ *  - All arrays are row-major and contiguous; device pointers must be
+ *    16-byte aligned.
+ *  - Calls that share a workspace must not overlap on different streams.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,          /* bad config value, NULL pointer, T < 0 */
+    MOE_ERR_UNSUPPORTED = -2,          /* valid config outside what the kernels handle */
+    MOE_ERR_WORKSPACE_TOO_SMALL = -3,
+    MOE_ERR_MISALIGNED = -4,           /* a device pointer not 16-byte aligned */
+    MOE_ERR_HIP = -5,                  /* a HIP launch error */
+    MOE_ERR_ABI_MISMATCH = -6          /* cfg->abi_version != MOE_ABI_VERSION */
+};
+
+/* Router score function. */
+enum moe_score_fn {
+    MOE_SCORE_SOFTMAX = 0,   /* select on logits; gates = softmax over the selected (or all) */
+    MOE_SCORE_SIGMOID = 1    /* s = sigmoid(logit); select on s + score_bias; gates from s */
+};
+
+/* Numeric format of weights and activations.
+ *  F32  : weights, hidden states, intermediate h and expert output rows fp32.
+ *  BF16 : weights, hidden states, h and expert output rows bf16; fp32 accumulate.
+ *  FP8  : expert weights e4m3fn with one fp32 scale per 128x128 block
+ *         (static); hidden states come in bf16 and are quantised to e4m3 with
+ *         one fp32 scale per 1x128 block before the gate/up GEMM, h likewise
+ *         before the down GEMM (dynamic); expert output rows bf16; the router
+ *         weight stays bf16. (Perplexity, section "Quantization".) */
+enum moe_dtype {
+    MOE_DTYPE_F32 = 0,
+    MOE_DTYPE_BF16 = 1,
+    MOE_DTYPE_FP8 = 2
+};
+
+typedef struct moe_config {
+    int32_t abi_version;     /* MOE_ABI_VERSION */
+    int32_t hidden;          /* H */
+    int32_t n_experts;       /* E, routed experts of the whole layer */
+    int32_t expert_begin;    /* local share [expert_begin, expert_end) of routed experts */
+    int32_t expert_end;
+    int32_t top_k;           /* k, experts per token (1..16) */
+    int32_t n_group;         /* G, expert groups (E % G == 0); 1 = no group limit */
+    int32_t topk_group;      /* G_k, groups kept per token (1..G) */
+    int32_t score_fn;        /* enum moe_score_fn */
+    int32_t renormalize;     /* 1: gates renormalised over the k selected */
+    float routed_scale;      /* gamma, multiplies every gate */
+    int32_t inter;           /* I, routed expert intermediate size */
+    int32_t shared_inter;    /* I_s, shared expert intermediate size; 0 = none */
+    int32_t dtype;           /* enum moe_dtype */
+    int32_t out_dtype;       /* MOE_DTYPE_F32 or MOE_DTYPE_BF16: layer output y */
+    float capacity_factor;   /* > 0: each local expert keeps at most
+                                ceil(cf * T * k / E) pairs, in token order */
+} moe_config;
+
+/* Expert weights, canonical nn.Linear (out x in) layout, local experts only.
+ *  w13       [E_l, 2I, H]: rows 0..I-1 gate, I..2I-1 up projection
+ *  w2        [E_l, H, I]:  down projection
+ *  shared_*  the same for the shared expert with I_s ([2 I_s, H], [H, I_s])
+ *  *_scale   FP8 only: fp32 [E_l, 2I/128, H/128], [E_l, H/128, I/128] and
+ *            [2 I_s/128, H/128], [H/128, I_s/128]; NULL otherwise. */
+typedef struct moe_weights {
+    const void* w13;
+    const void* w2;
+    const float* w13_scale;
+    const float* w2_scale;
+    const void* shared_w13;
+    const void* shared_w2;
+    const float* shared_w13_scale;
+    const float* shared_w2_scale;
+} moe_weights;
+
+int moe_abi_version(void);
+const char* moe_status_string(int status);
+
+/* Checks the config alone (host only): E % G == 0, E/G >= 2 when G > 1,
+ * 1 <= topk_group <= G, 1 <= k <= min(16, topk_group * E / G),
+ * 0 <= begin < end <= E, H % 128 == 0, I % 128 == 0, I_s % 128 == 0,
+ * E <= 512, E_l <= 1024. */
+int moe_validate_config(const moe_config* cfg);
+
+/* Bytes of workspace that moe_forward (and each stage call) needs for up to
+ * max_tokens tokens. Written to *bytes. */
+int moe_workspace_bytes(const moe_config* cfg, int64_t max_tokens, size_t* bytes);
+
+/* Router GEMM: logits[T, E] (fp32) = x[T, H] . w_router[E, H]^T + router_bias.
+ * x and w_router are fp32 (F32) or bf16 (BF16, FP8): inputs of the activation
+ * type in, fp32 out, no separate cast (NVIDIA, "MoE layer optimisations >
+ * mixed I/O RouterGEMM"). router_bias [E] fp32 may be NULL. All device. */
+int moe_router_gemm(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                    const float* router_bias, float* logits, hipStream_t stream);
+
+/* Scores and group-limited top-k (NVIDIA, "Top-K kernel fusion"; Perplexity,
+ * "MoE Router"; glossary, "Load balancing and capacity").
+ *  logits     [T, E] fp32 device, finite
+ *  score_bias [E] fp32 device or NULL: added to the score for selection only
+ *  topk_ids   [T, k] int32 device out: global expert ids, slot order =
+ *             descending selection score, ties to the lower expert id
+ *  topk_w     [T, k] fp32 device out: gates
+ * Group score = sum of the two largest selection scores in the group; the G_k
+ * best groups are kept (ties to the lower group). Sigmoid gates are
+ * s_j / sum_i s_i (unbiased scores, if renormalize) times routed_scale;
+ * softmax gates are exp(l_j - max) / sum over the selected (or all) experts.
+ * The float32 exp/sigmoid follow a fixed recipe (Cody-Waite reduction,
+ * degree-8 Taylor polynomial, ldexp; no fused multiply-add; correctly
+ * rounded division), so results are reproducible bit for bit. */
+int moe_route(const moe_config* cfg, int64_t T, const float* logits, const float* score_bias,
+              int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* Dispatch: a stable permutation of the (token, slot) pairs into
+ * expert-contiguous order for the local experts (Perplexity, "MoE Router":
+ * dense dispatch needs the routing aggregated per expert; glossary: capacity).
+ * Pairs p = t*k + j are taken in increasing p. All int32 device:
+ *  topk_ids   [T, k] in
+ *  raw_counts [E_l] out (may be NULL): local pairs per expert before capacity
+ *  counts     [E_l] out: kept rows per expert (min(raw, C))
+ *  offsets    [E_l + 1] out: exclusive prefix of counts; offsets[E_l] = R
+ *  perm       [T*k] out: perm[row] = p for rows 0..R-1 (rest untouched)
+ *  inv        [T*k] out: inv[p] = row, or -1 for non-local or dropped pairs
+ * An expert id outside [0, E) is treated as non-local. */
+int moe_dispatch(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int32_t* raw_counts,
+                 int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert FFNs as grouped GEMMs (Perplexity, "Roofline > GroupGEMM";
+ * infra guide section 2.1): for every row r of local expert e,
+ *   h = silu(x_t W_gate[e]^T) * (x_t W_up[e]^T),  out_rows[r] = h W_down[e]^T
+ * with t = perm[r] / k; and for every token, the shared expert's output in
+ * shared_out[t] (if shared_inter > 0). Group sizes are read from `offsets`
+ * on the device, so no host synchronisation is needed.
+ *  x          [T, H] device, activation type (bf16 for FP8)
+ *  perm, offsets  from moe_dispatch
+ *  out_rows   [T*k, H] device out (fp32 for F32, bf16 otherwise); rows >= R untouched
+ *  shared_out [T, H] device out, same type; required iff shared_inter > 0 */
+int moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const int32_t* perm,
+                   const int32_t* offsets, const moe_weights* weights, void* out_rows,
+                   void* shared_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Combine (glossary step 4; infra guide section 3.1 step 4):
+ *   y[t] = shared_out[t] + sum_j [inv[t,j] >= 0] * topk_w[t,j] * out_rows[inv[t,j]]
+ * summed in fp32; dropped and non-local pairs add nothing (no renormalisation).
+ * y [T, H] device out in cfg->out_dtype; shared_out may be NULL. */
+int moe_combine(const moe_config* cfg, int64_t T, const void* out_rows, const int32_t* inv,
+                const float* topk_w, const void* shared_out, void* y, hipStream_t stream);
+
+/* The whole layer: router GEMM, route, dispatch, experts, combine.
+ *  x [T, H], w_router [E, H] (activation type; bf16 for FP8), router_bias [E]
+ *  and score_bias [E] fp32 or NULL, weights as above; y [T, H] out.
+ *  logits_out [T, E] fp32 and topk_ids_out [T, k] int32, if not NULL, receive
+ *  the router logits and expert ids. */
+int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                const float* router_bias, const float* score_bias, const moe_weights* weights,
+                void* y, float* logits_out, int32_t* topk_ids_out,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- Diagnostics: per-stage timing with HIP events ------------------------
+ * Not part of the layer. moe_profile_enable(n) creates 2n HIP events and
+ * starts recording: from then on every stage of every call records a start
+ * and a stop event on its stream (at most n stages are recorded; later ones
+ * are not). moe_profile_enable(0) stops and destroys the events;
+ * moe_profile_reset() forgets what was recorded. moe_profile_query(stage)
+ * waits for the recorded events of that stage and returns their summed
+ * elapsed time and how many were recorded. Single-threaded use only. */
+enum moe_stage {
+    MOE_STAGE_ROUTER_GEMM = 0,
+    MOE_STAGE_ROUTE = 1,
+    MOE_STAGE_DISPATCH = 2,
+    MOE_STAGE_GATE_UP = 3,          /* routed experts: gate/up GEMM + SwiGLU */
+    MOE_STAGE_DOWN = 4,             /* routed experts: down GEMM */
+    MOE_STAGE_SHARED_GATE_UP = 5,
+    MOE_STAGE_SHARED_DOWN = 6,
+    MOE_STAGE_COMBINE = 7,
+    MOE_STAGE_COUNT = 8
+};
+int moe_profile_enable(int max_records);
+int moe_profile_reset(void);
+int moe_profile_query(int stage, double* total_ms, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

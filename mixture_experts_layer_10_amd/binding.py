@@ -1,0 +1,303 @@
+"""Thin ctypes binding of libmoe.so (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, checks
+dtype, shape, contiguity and device, and passes raw pointers and the current
+HIP stream to the C entry point of the same name; a nonzero status raises
+MoEError. Every step of the layer runs in the library's HIP kernels: there is
+no fallback. If libmoe.so is missing, importing the functions raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+ABI_VERSION = 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_MISALIGNED, ERR_HIP, ERR_ABI_MISMATCH = \
+    0, -1, -2, -3, -4, -5, -6
+SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8 = 0, 1, 2
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("expert_begin", ctypes.c_int32), ("expert_end", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32), ("score_fn", ctypes.c_int32),
+                ("renormalize", ctypes.c_int32), ("routed_scale", ctypes.c_float), ("inter", ctypes.c_int32),
+                ("shared_inter", ctypes.c_int32), ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_float)]
+
+    @property
+    def n_local(self):
+        return self.expert_end - self.expert_begin
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w13", "w2", "w13_scale", "w2_scale", "shared_w13", "shared_w2",
+                 "shared_w13_scale", "shared_w2_scale")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mixture_experts_layer_10_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32p, fp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+        cfgp = ctypes.POINTER(Config)
+        wp = ctypes.POINTER(Weights)
+        sig = {
+            "moe_abi_version": (ctypes.c_int, []),
+            "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "moe_validate_config": (ctypes.c_int, [cfgp]),
+            "moe_workspace_bytes": (ctypes.c_int, [cfgp, i64, ctypes.POINTER(ctypes.c_size_t)]),
+            "moe_router_gemm": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, vp]),
+            "moe_route": (ctypes.c_int, [cfgp, i64, fp, fp, i32p, fp, vp]),
+            "moe_dispatch": (ctypes.c_int, [cfgp, i64, i32p, i32p, i32p, i32p, i32p, i32p, vp, ctypes.c_size_t, vp]),
+            "moe_expert_ffn": (ctypes.c_int, [cfgp, i64, vp, i32p, i32p, wp, vp, vp, vp, ctypes.c_size_t, vp]),
+            "moe_combine": (ctypes.c_int, [cfgp, i64, vp, i32p, fp, vp, vp, vp]),
+            "moe_forward": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, wp, vp, fp, i32p, vp, ctypes.c_size_t, vp]),
+            "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+            "moe_profile_reset": (ctypes.c_int, []),
+            "moe_profile_query": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                                  ctypes.POINTER(ctypes.c_int)]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        if L.moe_abi_version() != ABI_VERSION:
+            raise ImportError("libmoe.so ABI version does not match the binding")
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().moe_status_string(status).decode()
+
+
+def _check(status, where):
+    if status != OK:
+        raise MoEError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# Configuration
+# ---------------------------------------------------------------------------
+
+_DT = {"f32": DTYPE_F32, "bf16": DTYPE_BF16, "fp8": DTYPE_FP8}
+
+
+def make_config(hidden, n_experts, top_k, inter, *, expert_begin=0, expert_end=None, n_group=1,
+                topk_group=1, score_fn="softmax", renormalize=True, routed_scale=1.0, shared_inter=0,
+                dtype="bf16", out_dtype="f32", capacity_factor=0.0):
+    c = Config()
+    c.abi_version = ABI_VERSION
+    c.hidden, c.n_experts, c.top_k, c.inter = hidden, n_experts, top_k, inter
+    c.expert_begin = expert_begin
+    c.expert_end = n_experts if expert_end is None else expert_end
+    c.n_group, c.topk_group = n_group, topk_group
+    c.score_fn = SCORE_SIGMOID if score_fn == "sigmoid" else SCORE_SOFTMAX
+    c.renormalize = 1 if renormalize else 0
+    c.routed_scale = routed_scale
+    c.shared_inter = shared_inter
+    c.dtype = _DT[dtype]
+    c.out_dtype = _DT[out_dtype]
+    c.capacity_factor = capacity_factor
+    return c
+
+
+def config_from_workload(w, out_dtype="f32"):
+    return make_config(w["hidden"], w["n_experts"], w["top_k"], w["inter"], expert_begin=w["expert_begin"],
+                       expert_end=w["expert_end"], n_group=w["n_group"], topk_group=w["topk_group"],
+                       score_fn=w["score_fn"], renormalize=w["renormalize"], routed_scale=w["routed_scale"],
+                       shared_inter=w["shared_inter"], dtype=w["dtype"], out_dtype=out_dtype,
+                       capacity_factor=w["capacity_factor"])
+
+
+def validate_config(cfg):
+    return lib().moe_validate_config(ctypes.byref(cfg))
+
+
+def workspace_bytes(cfg, max_tokens):
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_bytes(ctypes.byref(cfg), int(max_tokens), ctypes.byref(n)), "moe_workspace_bytes")
+    return n.value
+
+
+def workspace(cfg, max_tokens, device="cuda"):
+    """A caller-owned device workspace for up to max_tokens tokens."""
+    return torch.empty(max(workspace_bytes(cfg, max_tokens), 16), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# Pointer helpers
+# ---------------------------------------------------------------------------
+
+def _act_dtype(cfg):
+    return torch.float32 if cfg.dtype == DTYPE_F32 else torch.bfloat16
+
+
+def _row_dtype(cfg):
+    return torch.float32 if cfg.dtype == DTYPE_F32 else torch.bfloat16
+
+
+def _out_dtype(cfg):
+    return torch.float32 if cfg.out_dtype == DTYPE_F32 else torch.bfloat16
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor", optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _weight_dtype(cfg):
+    return torch.float8_e4m3fn if cfg.dtype == DTYPE_FP8 else _act_dtype(cfg)
+
+
+def make_weights(cfg, w13, w2, shared_w13=None, shared_w2=None, w13_scale=None, w2_scale=None,
+                 shared_w13_scale=None, shared_w2_scale=None):
+    """Pack weight tensor pointers (the tensors must outlive the calls)."""
+    El, H, I, Is = cfg.n_local, cfg.hidden, cfg.inter, cfg.shared_inter
+    wd = _weight_dtype(cfg)
+    W = Weights()
+    W.w13 = _ptr(w13, wd, (El, 2 * I, H), "w13")
+    W.w2 = _ptr(w2, wd, (El, H, I), "w2")
+    if Is > 0:
+        W.shared_w13 = _ptr(shared_w13, wd, (2 * Is, H), "shared_w13")
+        W.shared_w2 = _ptr(shared_w2, wd, (H, Is), "shared_w2")
+    if cfg.dtype == DTYPE_FP8:
+        f32 = torch.float32
+        W.w13_scale = _ptr(w13_scale, f32, (El, 2 * I // 128, H // 128), "w13_scale")
+        W.w2_scale = _ptr(w2_scale, f32, (El, H // 128, I // 128), "w2_scale")
+        if Is > 0:
+            W.shared_w13_scale = _ptr(shared_w13_scale, f32, (2 * Is // 128, H // 128), "shared_w13_scale")
+            W.shared_w2_scale = _ptr(shared_w2_scale, f32, (H // 128, Is // 128), "shared_w2_scale")
+    W._keep = (w13, w2, shared_w13, shared_w2, w13_scale, w2_scale, shared_w13_scale, shared_w2_scale)
+    return W
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def moe_router_gemm(cfg, x, w_router, router_bias, logits, stream=None):
+    T = x.shape[0]
+    _check(lib().moe_router_gemm(
+        ctypes.byref(cfg), T, _ptr(x, _act_dtype(cfg), (T, cfg.hidden), "x"),
+        _ptr(w_router, _act_dtype(cfg), (cfg.n_experts, cfg.hidden), "w_router"),
+        _ptr(router_bias, torch.float32, (cfg.n_experts,), "router_bias", optional=True),
+        _ptr(logits, torch.float32, (T, cfg.n_experts), "logits"), _stream(stream)), "moe_router_gemm")
+
+
+def moe_route(cfg, logits, score_bias, topk_ids, topk_w, stream=None):
+    T = logits.shape[0]
+    k = cfg.top_k
+    _check(lib().moe_route(
+        ctypes.byref(cfg), T, _ptr(logits, torch.float32, (T, cfg.n_experts), "logits"),
+        _ptr(score_bias, torch.float32, (cfg.n_experts,), "score_bias", optional=True),
+        _ptr(topk_ids, torch.int32, (T, k), "topk_ids"), _ptr(topk_w, torch.float32, (T, k), "topk_w"),
+        _stream(stream)), "moe_route")
+
+
+def moe_dispatch(cfg, topk_ids, raw_counts, counts, offsets, perm, inv, ws, stream=None):
+    T, k = topk_ids.shape
+    El = cfg.n_local
+    i32 = torch.int32
+    _check(lib().moe_dispatch(
+        ctypes.byref(cfg), T, _ptr(topk_ids, i32, (T, k), "topk_ids"),
+        _ptr(raw_counts, i32, (El,), "raw_counts", optional=True), _ptr(counts, i32, (El,), "counts"),
+        _ptr(offsets, i32, (El + 1,), "offsets"), _ptr(perm, i32, (T * k,), "perm"),
+        _ptr(inv, i32, (T * k,), "inv"), _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream)),
+        "moe_dispatch")
+
+
+def moe_expert_ffn(cfg, x, perm, offsets, weights, out_rows, shared_out, ws, stream=None):
+    T = x.shape[0]
+    k, H = cfg.top_k, cfg.hidden
+    rd = _row_dtype(cfg)
+    _check(lib().moe_expert_ffn(
+        ctypes.byref(cfg), T, _ptr(x, _act_dtype(cfg), (T, H), "x"), _ptr(perm, torch.int32, (T * k,), "perm"),
+        _ptr(offsets, torch.int32, (cfg.n_local + 1,), "offsets"), ctypes.byref(weights),
+        _ptr(out_rows, rd, (T * k, H), "out_rows"),
+        _ptr(shared_out, rd, (T, H), "shared_out", optional=cfg.shared_inter == 0),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_combine(cfg, out_rows, inv, topk_w, shared_out, y, stream=None):
+    T, H = y.shape
+    k = cfg.top_k
+    rd = _row_dtype(cfg)
+    _check(lib().moe_combine(
+        ctypes.byref(cfg), T, _ptr(out_rows, rd, None, "out_rows"), _ptr(inv, torch.int32, (T * k,), "inv"),
+        _ptr(topk_w, torch.float32, (T, k), "topk_w"), _ptr(shared_out, rd, (T, H), "shared_out", optional=True),
+        _ptr(y, _out_dtype(cfg), (T, H), "y"), _stream(stream)), "moe_combine")
+
+
+def moe_forward(cfg, x, w_router, router_bias, score_bias, weights, y, ws, logits_out=None,
+                topk_ids_out=None, stream=None):
+    T = x.shape[0]
+    H, E = cfg.hidden, cfg.n_experts
+    _check(lib().moe_forward(
+        ctypes.byref(cfg), T, _ptr(x, _act_dtype(cfg), (T, H), "x"),
+        _ptr(w_router, _act_dtype(cfg), (E, H), "w_router"),
+        _ptr(router_bias, torch.float32, (E,), "router_bias", optional=True),
+        _ptr(score_bias, torch.float32, (E,), "score_bias", optional=True), ctypes.byref(weights),
+        _ptr(y, _out_dtype(cfg), (T, H), "y"),
+        _ptr(logits_out, torch.float32, (T, E), "logits_out", optional=True),
+        _ptr(topk_ids_out, torch.int32, (T, cfg.top_k), "topk_ids_out", optional=True),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream)), "moe_forward")
+
+
+# ---------------------------------------------------------------------------
+# Diagnostics: per-stage HIP-event timing
+# ---------------------------------------------------------------------------
+
+STAGES = ["router_gemm", "route", "dispatch", "gate_up", "down", "shared_gate_up", "shared_down", "combine"]
+
+
+def profile_enable(max_records):
+    _check(lib().moe_profile_enable(int(max_records)), "moe_profile_enable")
+
+
+def profile_reset():
+    _check(lib().moe_profile_reset(), "moe_profile_reset")
+
+
+def profile_query():
+    """{stage: (total_ms, launches)} for every stage recorded since the last reset."""
+    out = {}
+    for i, name in enumerate(STAGES):
+        ms, n = ctypes.c_double(0), ctypes.c_int(0)
+        _check(lib().moe_profile_query(i, ctypes.byref(ms), ctypes.byref(n)), "moe_profile_query")
+        out[name] = (ms.value, n.value)
+    return out

@@ -1,0 +1,475 @@
+// The C ABI of libmoe.so: argument validation, workspace layout, and the
+// launch sequence of each stage. Host code only; kernels live in route.hip,
+// dispatch.hip, gemm.hip, quant.hip and combine.hip.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int validate(const moe_config* c) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->abi_version != MOE_ABI_VERSION) return MOE_ERR_ABI_MISMATCH;
+    if (c->hidden <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->inter <= 0 || c->shared_inter < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (c->n_group <= 0 || c->n_experts % c->n_group != 0) return MOE_ERR_INVALID_ARG;
+    if (c->topk_group <= 0 || c->topk_group > c->n_group) return MOE_ERR_INVALID_ARG;
+    if (c->top_k > c->topk_group * (c->n_experts / c->n_group)) return MOE_ERR_INVALID_ARG;
+    if (c->expert_begin < 0 || c->expert_end <= c->expert_begin || c->expert_end > c->n_experts)
+        return MOE_ERR_INVALID_ARG;
+    if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+    if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
+    if (!isfinite(c->routed_scale) || !isfinite(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
+    if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16 && c->dtype != MOE_DTYPE_FP8)
+        return MOE_ERR_INVALID_ARG;
+    if (c->out_dtype != MOE_DTYPE_F32 && c->out_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+    // Valid, but outside what the kernels are built for.
+    if (c->top_k > 16 || c->n_experts > 512 || c->n_group > 64) return MOE_ERR_UNSUPPORTED;
+    if (c->expert_end - c->expert_begin > 1024) return MOE_ERR_UNSUPPORTED;
+    if (c->hidden % 128 != 0 || c->inter % 128 != 0 || c->shared_inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if (c->dtype == MOE_DTYPE_FP8) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int act_bytes(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 4 : c->dtype == MOE_DTYPE_BF16 ? 2 : 1; }
+int row_bytes(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 4 : 2; }
+Elem gemm_elem(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? Elem::F32 : Elem::BF16; }
+
+// Workspace layout for up to T tokens; every region 256-byte aligned.
+struct Layout {
+    size_t logits, ids, w, raw, counts, offsets, perm, inv, chunk_hist, chunk_base, sched;
+    size_t h, h_shared, rows, shared_out, total;
+};
+
+Layout layout(const moe_config* c, int64_t T) {
+    const int64_t E = c->n_experts, El = c->expert_end - c->expert_begin, k = c->top_k;
+    const int64_t P = T * k;
+    const int64_t nchunk = dispatch_chunks(P);
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align_up(bytes);
+        return at;
+    };
+    L.logits = take(sizeof(float) * T * E);
+    L.ids = take(sizeof(int32_t) * P);
+    L.w = take(sizeof(float) * P);
+    L.raw = take(sizeof(int32_t) * El);
+    L.counts = take(sizeof(int32_t) * El);
+    L.offsets = take(sizeof(int32_t) * (El + 1));
+    L.perm = take(sizeof(int32_t) * P);
+    L.inv = take(sizeof(int32_t) * P);
+    L.chunk_hist = take(sizeof(int32_t) * nchunk * El);
+    L.chunk_base = take(sizeof(int32_t) * nchunk * El);
+    L.sched = take(sizeof(int32_t) * (El + 2));
+    L.h = take(static_cast<size_t>(act_bytes(c)) * P * c->inter);
+    L.h_shared = take(static_cast<size_t>(act_bytes(c)) * T * c->shared_inter);
+    L.rows = take(static_cast<size_t>(row_bytes(c)) * P * c->hidden);
+    L.shared_out = take(static_cast<size_t>(row_bytes(c)) * T * c->hidden);
+    L.total = off;
+    return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+    return reinterpret_cast<P*>(static_cast<unsigned char*>(ws) + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// ---- optional per-stage timing with HIP events (diagnostics only) ------------
+// Events are created by moe_profile_enable, never on a call path; while
+// enabled, each stage records a start and a stop event on its stream.
+struct Profiler {
+    bool on = false;
+    int cap = 0, n = 0;
+    std::vector<hipEvent_t> ev;   // 2 per record
+    std::vector<int> stage;
+} g_prof;
+
+struct StageTimer {
+    int stage;
+    hipStream_t s;
+    bool active;
+    StageTimer(int st, hipStream_t str) : stage(st), s(str), active(g_prof.on && g_prof.n < g_prof.cap) {
+        if (active) {
+            g_prof.stage[g_prof.n] = stage;
+            hipEventRecord(g_prof.ev[2 * g_prof.n], s);
+        }
+    }
+    ~StageTimer() {
+        if (active) {
+            hipEventRecord(g_prof.ev[2 * g_prof.n + 1], s);
+            ++g_prof.n;
+        }
+    }
+};
+
+int check_ws(const moe_config* c, int64_t T, const void* ws, size_t ws_bytes) {
+    if (!ws) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+    if (ws_bytes < layout(c, T).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return MOE_OK;
+}
+
+int64_t capacity_of(const moe_config* c, int64_t T) {
+    if (!(c->capacity_factor > 0.0f)) return INT64_MAX;
+    return static_cast<int64_t>(ceil(static_cast<double>(c->capacity_factor) * static_cast<double>(T) *
+                                     static_cast<double>(c->top_k) / static_cast<double>(c->n_experts)));
+}
+
+// ---- stage bodies (arguments already validated) ------------------------------
+
+hipError_t do_router_gemm(const moe_config* c, int64_t T, const void* x, const void* wr, const float* bias,
+                          float* logits, hipStream_t s) {
+    StageTimer tm(MOE_STAGE_ROUTER_GEMM, s);
+    GemmArgs g{};
+    g.A = g.A_shared = x;
+    g.B = g.B_shared = wr;
+    g.n_local = 1;
+    g.T = static_cast<int>(T);
+    g.K = c->hidden;
+    g.N = c->n_experts;
+    g.C = g.C_shared = logits;
+    g.ldc = c->n_experts;
+    g.bias = bias;
+    g.out_f32 = 1;
+    const GemmPlan p = plan_gemm(gemm_elem(c), Epi::PLAIN, T, 1, T, c->n_experts);
+    return launch_gemm(gemm_elem(c), Epi::PLAIN, g, p, s);
+}
+
+hipError_t do_route(const moe_config* c, int64_t T, const float* logits, const float* sbias, int32_t* ids,
+                    float* w, hipStream_t s) {
+    StageTimer tm(MOE_STAGE_ROUTE, s);
+    RouteArgs r{};
+    r.logits = logits;
+    r.score_bias = sbias;
+    r.ids = ids;
+    r.w = w;
+    r.T = static_cast<int>(T);
+    r.E = c->n_experts;
+    r.k = c->top_k;
+    r.G = c->n_group;
+    r.Gk = c->topk_group;
+    r.score_fn = c->score_fn;
+    r.renorm = c->renormalize;
+    r.gamma = c->routed_scale;
+    return launch_route(r, s);
+}
+
+hipError_t do_dispatch(const moe_config* c, int64_t T, const int32_t* ids, int32_t* raw, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* inv, void* ws, hipStream_t s) {
+    StageTimer tm(MOE_STAGE_DISPATCH, s);
+    const Layout L = layout(c, T);
+    DispatchArgs d{};
+    d.ids = ids;
+    d.raw = raw;
+    d.counts = counts;
+    d.offsets = offsets;
+    d.perm = perm;
+    d.inv = inv;
+    d.chunk_hist = at<int32_t>(ws, L.chunk_hist);
+    d.chunk_base = at<int32_t>(ws, L.chunk_base);
+    d.P = T * c->top_k;
+    d.E = c->n_experts;
+    d.El = c->expert_end - c->expert_begin;
+    d.begin = c->expert_begin;
+    d.cap = capacity_of(c, T);
+    return launch_dispatch(d, s);
+}
+
+hipError_t do_expert_ffn(const moe_config* c, int64_t T, const void* x, const int32_t* perm,
+                         const int32_t* offsets, const moe_weights* wt, void* rows, void* shared_out, void* ws,
+                         hipStream_t s) {
+    const Layout L = layout(c, T);
+    const Elem el = gemm_elem(c);
+    const int El = c->expert_end - c->expert_begin;
+    const int64_t H = c->hidden, I = c->inter, Is = c->shared_inter;
+    const int64_t P = T * c->top_k;
+    int32_t* sched = at<int32_t>(ws, L.sched);
+    hipError_t e;
+
+    // Routed experts: gate/up GEMM with fused SwiGLU, then the down GEMM.
+    GemmArgs g1{};
+    g1.A = g1.A_shared = x;
+    g1.perm = perm;
+    g1.gather = 1;
+    g1.topk = c->top_k;
+    g1.B = g1.B_shared = wt->w13;
+    g1.b_stride = 2 * I * H;
+    g1.offsets = offsets;
+    g1.sched = sched;
+    g1.n_local = El;
+    g1.T = static_cast<int>(T);
+    g1.K = static_cast<int>(H);
+    g1.N = static_cast<int>(I);
+    g1.inter = static_cast<int>(I);
+    g1.C = g1.C_shared = at<void>(ws, L.h);
+    g1.ldc = static_cast<int>(I);
+    const int64_t per_expert = (P + c->n_experts - 1) / c->n_experts;
+    const GemmPlan p1 = plan_gemm(el, Epi::SWIGLU, P, El, per_expert, static_cast<int>(I));
+    if ((e = launch_schedule(g1, p1.bm, sched, s)) != hipSuccess) return e;
+    {
+        StageTimer tm(MOE_STAGE_GATE_UP, s);
+        if ((e = launch_gemm(el, Epi::SWIGLU, g1, p1, s)) != hipSuccess) return e;
+    }
+
+    GemmArgs g2 = g1;
+    g2.A = g2.A_shared = at<void>(ws, L.h);
+    g2.perm = nullptr;
+    g2.gather = 0;
+    g2.B = g2.B_shared = wt->w2;
+    g2.b_stride = H * I;
+    g2.K = static_cast<int>(I);
+    g2.N = static_cast<int>(H);
+    g2.inter = 0;
+    g2.C = g2.C_shared = rows;
+    g2.ldc = static_cast<int>(H);
+    g2.out_f32 = c->dtype == MOE_DTYPE_F32;
+    GemmPlan p2 = plan_gemm(el, Epi::PLAIN, P, El, per_expert, static_cast<int>(H));
+    p2.bm = p1.bm;       // same m-tiles as the schedule
+    p2.grid = ((P / p2.bm + El) * p2.n_tiles + 7) / 8 * 8;
+    {
+        StageTimer tm(MOE_STAGE_DOWN, s);
+        if ((e = launch_gemm(el, Epi::PLAIN, g2, p2, s)) != hipSuccess) return e;
+    }
+
+    // Shared expert: every token, a single group (no schedule needed).
+    if (Is > 0) {
+        GemmArgs s1{};
+        s1.A = s1.A_shared = x;
+        s1.B = s1.B_shared = wt->shared_w13;
+        s1.n_local = 0;
+        s1.has_shared = 1;
+        s1.T = static_cast<int>(T);
+        s1.K = static_cast<int>(H);
+        s1.N = static_cast<int>(Is);
+        s1.inter = static_cast<int>(Is);
+        s1.C = s1.C_shared = at<void>(ws, L.h_shared);
+        s1.ldc = static_cast<int>(Is);
+        const GemmPlan q1 = plan_gemm(el, Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
+        {
+            StageTimer tm(MOE_STAGE_SHARED_GATE_UP, s);
+            if ((e = launch_gemm(el, Epi::SWIGLU, s1, q1, s)) != hipSuccess) return e;
+        }
+        GemmArgs s2 = s1;
+        s2.A = s2.A_shared = at<void>(ws, L.h_shared);
+        s2.B = s2.B_shared = wt->shared_w2;
+        s2.K = static_cast<int>(Is);
+        s2.N = static_cast<int>(H);
+        s2.inter = 0;
+        s2.C = s2.C_shared = shared_out;
+        s2.ldc = static_cast<int>(H);
+        s2.out_f32 = c->dtype == MOE_DTYPE_F32;
+        const GemmPlan q2 = plan_gemm(el, Epi::PLAIN, T, 1, T, static_cast<int>(H));
+        StageTimer tm(MOE_STAGE_SHARED_DOWN, s);
+        if ((e = launch_gemm(el, Epi::PLAIN, s2, q2, s)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t do_combine(const moe_config* c, int64_t T, const void* rows, const int32_t* inv, const float* w,
+                      const void* shared_out, void* y, hipStream_t s) {
+    StageTimer tm(MOE_STAGE_COMBINE, s);
+    CombineArgs a{};
+    a.rows = rows;
+    a.inv = inv;
+    a.w = w;
+    a.shared = shared_out;
+    a.y = y;
+    a.T = T;
+    a.H = c->hidden;
+    a.k = c->top_k;
+    a.rows_f32 = c->dtype == MOE_DTYPE_F32;
+    a.out_f32 = c->out_dtype == MOE_DTYPE_F32;
+    return launch_combine(a, s);
+}
+
+bool weights_ok(const moe_config* c, const moe_weights* w) {
+    if (!w || !w->w13 || !w->w2) return false;
+    if (!aligned16(w->w13) || !aligned16(w->w2)) return false;
+    if (c->shared_inter > 0 && (!w->shared_w13 || !w->shared_w2 || !aligned16(w->shared_w13) ||
+                                !aligned16(w->shared_w2)))
+        return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MOE_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+        case MOE_ERR_HIP: return "HIP launch error";
+        case MOE_ERR_ABI_MISMATCH: return "ABI version mismatch";
+        default: return "unknown status";
+    }
+}
+
+int moe_validate_config(const moe_config* cfg) { return validate(cfg); }
+
+int moe_workspace_bytes(const moe_config* cfg, int64_t max_tokens, size_t* bytes) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (max_tokens < 0 || !bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = layout(cfg, max_tokens).total;
+    return MOE_OK;
+}
+
+int moe_router_gemm(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* router_bias,
+                    float* logits, hipStream_t stream) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (T < 0 || T > INT32_MAX / 16) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits)) return MOE_ERR_MISALIGNED;
+    return hip_status(do_router_gemm(cfg, T, x, w_router, router_bias, logits, stream));
+}
+
+int moe_route(const moe_config* cfg, int64_t T, const float* logits, const float* score_bias, int32_t* topk_ids,
+              float* topk_w, hipStream_t stream) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (T < 0 || T > INT32_MAX / 16) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOE_ERR_MISALIGNED;
+    return hip_status(do_route(cfg, T, logits, score_bias, topk_ids, topk_w, stream));
+}
+
+int moe_dispatch(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int32_t* raw_counts, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (T < 0 || T > INT32_MAX / 16) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!topk_ids || !counts || !offsets || !perm || !inv) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(topk_ids) || !aligned16(counts) || !aligned16(offsets) || !aligned16(perm) || !aligned16(inv) ||
+        (raw_counts && !aligned16(raw_counts)))
+        return MOE_ERR_MISALIGNED;
+    if ((st = check_ws(cfg, T, ws, ws_bytes))) return st;
+    return hip_status(do_dispatch(cfg, T, topk_ids, raw_counts, counts, offsets, perm, inv, ws, stream));
+}
+
+int moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const int32_t* perm, const int32_t* offsets,
+                   const moe_weights* weights, void* out_rows, void* shared_out, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (T < 0 || T > INT32_MAX / 16) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !perm || !offsets || !out_rows || !weights_ok(cfg, weights)) return MOE_ERR_INVALID_ARG;
+    if (cfg->shared_inter > 0 && !shared_out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(perm) || !aligned16(offsets) || !aligned16(out_rows) ||
+        (shared_out && !aligned16(shared_out)))
+        return MOE_ERR_MISALIGNED;
+    if ((st = check_ws(cfg, T, ws, ws_bytes))) return st;
+    return hip_status(do_expert_ffn(cfg, T, x, perm, offsets, weights, out_rows, shared_out, ws, stream));
+}
+
+int moe_combine(const moe_config* cfg, int64_t T, const void* out_rows, const int32_t* inv, const float* topk_w,
+                const void* shared_out, void* y, hipStream_t stream) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (T < 0 || T > INT32_MAX / 16) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!out_rows || !inv || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(out_rows) || !aligned16(inv) || !aligned16(topk_w) || !aligned16(y) ||
+        (shared_out && !aligned16(shared_out)))
+        return MOE_ERR_MISALIGNED;
+    return hip_status(do_combine(cfg, T, out_rows, inv, topk_w, shared_out, y, stream));
+}
+
+int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* router_bias,
+                const float* score_bias, const moe_weights* weights, void* y, float* logits_out,
+                int32_t* topk_ids_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (T < 0 || T > INT32_MAX / 16) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !y || !weights_ok(cfg, weights)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(y) || (logits_out && !aligned16(logits_out)) ||
+        (topk_ids_out && !aligned16(topk_ids_out)))
+        return MOE_ERR_MISALIGNED;
+    if ((st = check_ws(cfg, T, ws, ws_bytes))) return st;
+    const Layout L = layout(cfg, T);
+    float* logits = logits_out ? logits_out : at<float>(ws, L.logits);
+    int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+    float* w = at<float>(ws, L.w);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* inv = at<int32_t>(ws, L.inv);
+    void* rows = at<void>(ws, L.rows);
+    void* shared_out = cfg->shared_inter > 0 ? at<void>(ws, L.shared_out) : nullptr;
+    hipError_t e;
+    if ((e = do_router_gemm(cfg, T, x, w_router, router_bias, logits, stream)) != hipSuccess) return MOE_ERR_HIP;
+    if ((e = do_route(cfg, T, logits, score_bias, ids, w, stream)) != hipSuccess) return MOE_ERR_HIP;
+    if ((e = do_dispatch(cfg, T, ids, at<int32_t>(ws, L.raw), at<int32_t>(ws, L.counts), offsets, perm, inv, ws,
+                         stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    if ((e = do_expert_ffn(cfg, T, x, perm, offsets, weights, rows, shared_out, ws, stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    if ((e = do_combine(cfg, T, rows, inv, w, shared_out, y, stream)) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_profile_enable(int max_records) {
+    if (max_records < 0) return MOE_ERR_INVALID_ARG;
+    for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
+    g_prof = Profiler{};
+    if (max_records == 0) return MOE_OK;
+    g_prof.ev.resize(2 * static_cast<size_t>(max_records));
+    g_prof.stage.resize(max_records);
+    for (auto& e : g_prof.ev)
+        if (hipEventCreate(&e) != hipSuccess) return MOE_ERR_HIP;
+    g_prof.cap = max_records;
+    g_prof.on = true;
+    return MOE_OK;
+}
+
+int moe_profile_reset(void) {
+    g_prof.n = 0;
+    return MOE_OK;
+}
+
+int moe_profile_query(int stage, double* total_ms, int* count) {
+    if (!total_ms || !count || stage < 0 || stage >= MOE_STAGE_COUNT) return MOE_ERR_INVALID_ARG;
+    double tot = 0.0;
+    int cnt = 0;
+    for (int i = 0; i < g_prof.n; ++i) {
+        if (g_prof.stage[i] != stage) continue;
+        if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) return MOE_ERR_HIP;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) return MOE_ERR_HIP;
+        tot += ms;
+        ++cnt;
+    }
+    *total_ms = tot;
+    *count = cnt;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Internal interface between the C ABI (moe_api.cpp) and the kernel
+// translation units. Host-side launch functions; each returns a hipError_t.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Element formats of the grouped GEMM operands.
+enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2 };
+
+// --- router (K2) -------------------------------------------------------------
+struct RouteArgs {
+    const float* logits;      // [T, E]
+    const float* score_bias;  // [E] or null
+    int32_t* ids;             // [T, k]
+    float* w;                 // [T, k]
+    int T, E, k, G, Gk, score_fn, renorm;
+    float gamma;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+// --- dispatch (K3) -----------------------------------------------------------
+constexpr int kDispatchChunk = 2048;     // pairs per block
+struct DispatchArgs {
+    const int32_t* ids;       // [P]
+    int32_t* raw;             // [El] or null
+    int32_t* counts;          // [El]
+    int32_t* offsets;         // [El + 1]
+    int32_t* perm;            // [P]
+    int32_t* inv;             // [P]
+    int32_t* chunk_hist;      // [nchunk, El] scratch
+    int32_t* chunk_base;      // [nchunk, El] scratch
+    int64_t P;                // T * k
+    int E, El, begin;
+    int64_t cap;              // capacity, or INT64_MAX
+};
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+inline int64_t dispatch_chunks(int64_t P) { return (P + kDispatchChunk - 1) / kDispatchChunk; }
+
+// --- grouped GEMM (K1, K5, K6) ----------------------------------------------
+enum class Epi : int { SWIGLU = 0, PLAIN = 1 };
+
+struct GemmArgs {
+    // A operand: routed rows (gathered through perm when gather != 0) and
+    // shared-expert rows (token t = row).
+    const void* A;            // routed-row source
+    const void* A_shared;     // shared-row source (may equal A)
+    const float* A_scale;     // FP8: [rows, K/128] scales of A (routed source)
+    const float* A_scale_shared;
+    const int32_t* perm;      // gather: token = perm[row] / topk
+    int gather;
+    int topk;
+    // B operand: [n_local, N_B, K] routed weights, [N_B, K] shared weights.
+    const void* B;
+    const void* B_shared;
+    const float* B_scale;     // FP8: [n_local, N_B/128, K/128]
+    const float* B_scale_shared;
+    int64_t b_stride;         // elements between routed experts
+    // Groups: rows of routed group g are offsets[g] .. offsets[g+1]-1;
+    // group n_local (if has_shared) has T rows.
+    const int32_t* offsets;   // [n_local + 1], or null for a single dense group
+    const int32_t* sched;     // [n_groups + 1] m-tile prefix
+    int n_local, has_shared, T;
+    int K;                    // reduction length
+    int N;                    // output columns (I for SWIGLU, else N_B)
+    int inter;                // SWIGLU: row offset of the up projection in B
+    // Outputs
+    void* C;                  // routed rows [rows, ldc]
+    void* C_shared;           // shared rows [T, ldc]
+    float* C_scale;           // FP8 SWIGLU: [rows, N/128]
+    float* C_scale_shared;
+    int ldc;
+    const float* bias;        // PLAIN fp32 out: per-column bias or null
+    int out_f32;              // PLAIN: 1 -> fp32 output, 0 -> bf16 output
+};
+
+struct GemmPlan {
+    int bm;                   // rows per tile
+    int n_tiles;              // column tiles per group
+    int64_t grid;             // workgroups launched (upper bound on tiles)
+};
+GemmPlan plan_gemm(Elem e, Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N);
+hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_t s);
+hipError_t launch_gemm(Elem e, Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
+
+// --- activation quantisation (K4) -------------------------------------------
+hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* q, float* scale, int64_t rows, int cols, hipStream_t s);
+
+// --- combine (K7) ------------------------------------------------------------
+struct CombineArgs {
+    const void* rows;         // [R, H]
+    const int32_t* inv;       // [T, k]
+    const float* w;           // [T, k]
+    const void* shared;       // [T, H] or null
+    void* y;                  // [T, H]
+    int64_t T;
+    int H, k;
+    int rows_f32;             // rows/shared are fp32 (else bf16)
+    int out_f32;              // y is fp32 (else bf16)
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

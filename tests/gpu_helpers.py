@@ -1,0 +1,90 @@
+"""Shared helpers of the GPU parity tests: run the HIP path stage by stage
+through the C ABI, and compare with the oracle on the same inputs."""
+import sys
+
+import numpy as np
+import torch
+
+import mixture_experts_layer_10_amd as moe
+from oracle import moe_oracle as O
+from synth import make_inputs
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    """torch tensor -> numpy (float values, or uint8 codes for float8)."""
+    if t is None:
+        return None
+    t = t.detach().cpu()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.float().numpy()
+    return t.numpy()
+
+
+class Run:
+    """Inputs of workload `w` on the GPU and the outputs of each HIP stage."""
+
+    def __init__(self, w, out_dtype="f32", gen_device="cpu", seed=0):
+        self.w = w
+        self.cfg = moe.config_from_workload(w, out_dtype=out_dtype)
+        self.ocfg = O.Config.from_workload(w)
+        inp = make_inputs(w, device=gen_device, seed=seed)
+        self.inp = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+        self.T = w["T"]
+        self.ws = moe.workspace(self.cfg, self.T)
+        i = self.inp
+        self.W = moe.make_weights(self.cfg, i["w13"], i["w2"], i["shared_w13"], i["shared_w2"],
+                                  i.get("w13_scale"), i.get("w2_scale"), i.get("shared_w13_scale"),
+                                  i.get("shared_w2_scale"))
+
+    def stages(self):
+        c, i, T = self.cfg, self.inp, self.T
+        E, k, El, H = c.n_experts, c.top_k, c.n_local, c.hidden
+        dev = "cuda"
+        r = {}
+        r["logits"] = torch.empty(T, E, dtype=torch.float32, device=dev)
+        moe.moe_router_gemm(c, i["x"], i["w_router"], i["router_bias"], r["logits"])
+        r["ids"] = torch.empty(T, k, dtype=torch.int32, device=dev)
+        r["w"] = torch.empty(T, k, dtype=torch.float32, device=dev)
+        moe.moe_route(c, r["logits"], i["score_bias"], r["ids"], r["w"])
+        r["raw_counts"] = torch.empty(El, dtype=torch.int32, device=dev)
+        r["counts"] = torch.empty(El, dtype=torch.int32, device=dev)
+        r["offsets"] = torch.empty(El + 1, dtype=torch.int32, device=dev)
+        r["perm"] = torch.full((T * k,), -7, dtype=torch.int32, device=dev)
+        r["inv"] = torch.empty(T * k, dtype=torch.int32, device=dev)
+        moe.moe_dispatch(c, r["ids"], r["raw_counts"], r["counts"], r["offsets"], r["perm"], r["inv"], self.ws)
+        rd = torch.float32 if c.dtype == moe.DTYPE_F32 else torch.bfloat16
+        r["rows"] = torch.zeros(T * k, H, dtype=rd, device=dev)
+        r["shared"] = torch.zeros(T, H, dtype=rd, device=dev) if c.shared_inter else None
+        moe.moe_expert_ffn(c, i["x"], r["perm"], r["offsets"], self.W, r["rows"], r["shared"], self.ws)
+        od = torch.float32 if c.out_dtype == moe.DTYPE_F32 else torch.bfloat16
+        r["y"] = torch.empty(T, H, dtype=od, device=dev)
+        moe.moe_combine(c, r["rows"], r["inv"], r["w"], r["shared"], r["y"])
+        torch.cuda.synchronize()
+        return r
+
+    def forward(self, y=None, logits_out=None, ids_out=None):
+        c, i = self.cfg, self.inp
+        od = torch.float32 if c.out_dtype == moe.DTYPE_F32 else torch.bfloat16
+        if y is None:
+            y = torch.empty(self.T, c.hidden, dtype=od, device="cuda")
+        moe.moe_forward(c, i["x"], i["w_router"], i["router_bias"], i["score_bias"], self.W, y, self.ws,
+                        logits_out=logits_out, topk_ids_out=ids_out)
+        return y
+
+    def oracle_forward(self, logits):
+        """Oracle layer output given the GPU's logits (whole batch)."""
+        i = self.inp
+        scales = {k: host(i.get(k)) for k in ("w13_scale", "w2_scale", "shared_w13_scale", "shared_w2_scale")}
+        return O.forward(self.ocfg, host(i["x"]), host(i["w_router"]), host(i["w13"]), host(i["w2"]),
+                         router_bias=host(i["router_bias"]), score_bias=host(i["score_bias"]),
+                         shared_w13=host(i["shared_w13"]), shared_w2=host(i["shared_w2"]),
+                         logits=host(logits), scales=scales)

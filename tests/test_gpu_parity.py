@@ -1,0 +1,248 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Routing ids and gates, counts, offsets, permutation and inverse permutation
+are compared bit for bit, with both sides given the same logits; layer
+outputs within max|dy| / RMS(y_oracle) <= 1e-5 (fp32), 2e-2 (bf16).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_10_amd as moe
+from oracle import moe_oracle as O
+from synth import workload
+
+from gpu_helpers import TOL, Run, host, say
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+def _small(**kw):
+    """A reduced DeepSeek-style layer: fast for the oracle, several tiles, ragged tails."""
+    w = dict(T=96, hidden=512, n_experts=64, expert_begin=0, expert_end=64, top_k=6, n_group=8,
+             topk_group=4, score_fn="sigmoid", renormalize=True, routed_scale=1.0, inter=256,
+             shared_inter=256, dtype="bf16", capacity_factor=0.0, score_bias="normal0.1",
+             router_bias="none")
+    w.update(kw)
+    w.setdefault("name", "small")
+    return w
+
+
+# ---------------------------------------------------------------------------
+# Router: bit-exact ids and gates from the same logits
+# ---------------------------------------------------------------------------
+
+def _adversarial_logits(T, E, rng):
+    l = rng.standard_normal((T, E)).astype(F32)
+    l[0] = 0.0                                   # all equal
+    l[1] = -0.0
+    l[2, ::2] = -0.0                              # +0 / -0 mix
+    l[3] = np.round(l[3] * 2) / 2                 # many exact ties
+    l[4] = 60.0 * np.sign(l[4])                   # saturated sigmoid
+    l[5] = rng.choice([-100.0, 100.0, -87.5], E)  # beyond the exp clamp
+    l[6] = rng.choice([1e-40, -1e-40, 1e-38], E).astype(F32)   # subnormals
+    l[7] = np.tile(np.arange(E // 8, dtype=F32), 8)            # equal group sums
+    return l
+
+
+ROUTE_CASES = [
+    dict(n_experts=8, top_k=2, n_group=1, topk_group=1, score_fn="softmax"),
+    dict(n_experts=256, top_k=8, n_group=8, topk_group=4, score_fn="sigmoid", bias=True),
+    dict(n_experts=256, top_k=8, n_group=8, topk_group=4, score_fn="sigmoid"),
+    dict(n_experts=64, top_k=6, n_group=8, topk_group=8, score_fn="sigmoid", bias=True),
+    dict(n_experts=16, top_k=16, n_group=1, topk_group=1, score_fn="softmax", renormalize=False),
+    dict(n_experts=32, top_k=4, n_group=4, topk_group=2, score_fn="softmax", routed_scale=2.5),
+    dict(n_experts=512, top_k=8, n_group=16, topk_group=4, score_fn="sigmoid", bias=True),
+    dict(n_experts=96, top_k=3, n_group=32, topk_group=3, score_fn="sigmoid", renormalize=False),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=lambda c: f"E{c['n_experts']}k{c['top_k']}{c['score_fn']}")
+def test_route_bit_exact(case):
+    case = dict(case)
+    bias = case.pop("bias", False)
+    rng = np.random.default_rng(case["n_experts"] + case["top_k"])
+    E = case["n_experts"]
+    T = 777
+    logits = _adversarial_logits(T, E, rng)
+    sb = (rng.standard_normal(E) * 0.1).astype(F32) if bias else None
+    cfg = moe.make_config(512, E, case["top_k"], 128, n_group=case["n_group"], topk_group=case["topk_group"],
+                          score_fn=case["score_fn"], renormalize=case.get("renormalize", True),
+                          routed_scale=case.get("routed_scale", 1.0), dtype="bf16")
+    say("route case", case, "T", T)
+    ids = torch.empty(T, case["top_k"], dtype=torch.int32, device="cuda")
+    w = torch.empty(T, case["top_k"], dtype=torch.float32, device="cuda")
+    moe.moe_route(cfg, torch.from_numpy(logits).cuda(), None if sb is None else torch.from_numpy(sb).cuda(), ids, w)
+    ocfg = O.Config(hidden=512, n_experts=E, top_k=case["top_k"], inter=128, n_group=case["n_group"],
+                    topk_group=case["topk_group"], score_fn=case["score_fn"],
+                    renormalize=case.get("renormalize", True), routed_scale=case.get("routed_scale", 1.0))
+    oid, ow = O.route(ocfg, logits, sb)
+    gid, gw = host(ids), host(w)
+    assert np.array_equal(gid, oid), np.argwhere(gid != oid)[:5]
+    assert np.array_equal(gw.view(np.int32), ow.view(np.int32)), np.argwhere(gw != ow)[:5]
+
+
+def test_sigmoid_recipe_bit_exact_sweep():
+    """The GPU's float32 sigmoid equals the oracle's on a sweep of inputs,
+    seen through the gates of a k = 1, no-renormalisation router."""
+    xs = np.concatenate([np.linspace(-90, 90, 200001, dtype=F32),
+                         (np.arange(0, 2 ** 31, 2 ** 15, dtype=np.int64).astype(np.uint32)).view(F32)])
+    xs = xs[np.isfinite(xs) & (np.abs(xs) < 1e30)].astype(F32)
+    xs = np.concatenate([xs, -xs])
+    n = len(xs)
+    E = 64
+    logits = np.full((n, E), -1e30, dtype=F32)
+    logits[:, 0] = xs
+    cfg = moe.make_config(512, E, 1, 128, score_fn="sigmoid", renormalize=False, dtype="bf16")
+    ids = torch.empty(n, 1, dtype=torch.int32, device="cuda")
+    w = torch.empty(n, 1, dtype=torch.float32, device="cuda")
+    moe.moe_route(cfg, torch.from_numpy(logits).cuda(), None, ids, w)
+    assert np.all(host(ids)[:, 0] == 0)
+    ref = O.sigmoid_f32(xs)
+    assert np.array_equal(host(w)[:, 0].view(np.int32), ref.view(np.int32))
+
+
+# ---------------------------------------------------------------------------
+# Dispatch: bit-exact counts, offsets, perm, inv; deterministic
+# ---------------------------------------------------------------------------
+
+def _ids(T, E, k, rng, skew):
+    p = np.exp(-skew * np.log(np.arange(1, E + 1)))
+    p = p / p.sum()
+    g = rng.random((T, E)) ** (1.0 / p)          # weighted sampling without replacement
+    return np.argsort(-g, axis=1)[:, :k].astype(np.int32)
+
+
+DISPATCH_CASES = [
+    (2048, 8, 2, 0, 8, 0.0, 0.0),
+    (2048, 256, 8, 0, 32, 0.0, 0.0),         # EP8 share
+    (512, 256, 8, 0, 256, 0.0, 0.0),
+    (8192, 256, 8, 0, 256, 1.25, 1.1),       # capacity with Zipf skew
+    (16384, 256, 8, 0, 256, 0.0, 0.0),
+    (3, 64, 6, 16, 48, 0.0, 0.0),            # ragged, tiny
+    (1, 256, 8, 0, 256, 0.0, 0.0),
+    (777, 64, 4, 60, 64, 1.0, 2.0),          # small share at the end, capacity
+    (5000, 512, 4, 0, 512, 0.0, 0.5),        # widest expert count
+]
+
+
+@pytest.mark.parametrize("T,E,k,b,e,cf,skew", DISPATCH_CASES)
+def test_dispatch_bit_exact(T, E, k, b, e, cf, skew):
+    rng = np.random.default_rng(T * 7 + E)
+    ids = _ids(T, E, k, rng, skew)
+    say("dispatch case", T, E, k, b, e, cf)
+    cfg = moe.make_config(512, E, k, 128, expert_begin=b, expert_end=e, dtype="bf16", capacity_factor=cf)
+    ocfg = O.Config(hidden=512, n_experts=E, top_k=k, inter=128, expert_begin=b, expert_end=e,
+                    capacity_factor=cf)
+    ref = O.dispatch(ocfg, ids)
+    El = e - b
+    dids = torch.from_numpy(ids).cuda()
+    ws = moe.workspace(cfg, T)
+    outs = []
+    for rep in range(20 if T >= 2048 else 3):
+        o = dict(raw_counts=torch.empty(El, dtype=torch.int32, device="cuda"),
+                 counts=torch.empty(El, dtype=torch.int32, device="cuda"),
+                 offsets=torch.empty(El + 1, dtype=torch.int32, device="cuda"),
+                 perm=torch.full((T * k,), -7, dtype=torch.int32, device="cuda"),
+                 inv=torch.empty(T * k, dtype=torch.int32, device="cuda"))
+        moe.moe_dispatch(cfg, dids, o["raw_counts"], o["counts"], o["offsets"], o["perm"], o["inv"], ws)
+        outs.append({k2: host(v) for k2, v in o.items()})
+    R = int(ref["offsets"][-1])
+    for o in outs:
+        for key in ("raw_counts", "counts", "offsets", "inv"):
+            assert np.array_equal(o[key], ref[key]), key
+        assert np.array_equal(o["perm"][:R], ref["perm"])
+        assert np.all(o["perm"][R:] == -7)          # rows past R untouched
+
+
+# ---------------------------------------------------------------------------
+# Router GEMM, experts, combine, whole layer
+# ---------------------------------------------------------------------------
+
+LAYER_CASES = {
+    "toy_fp32": lambda: workload("toy_fp32"),
+    "toy_fp32_ragged": lambda: workload("toy_fp32", T=77),
+    "small_bf16": lambda: _small(),
+    "small_bf16_share": lambda: _small(expert_begin=16, expert_end=40, T=333),
+    "small_bf16_capacity": lambda: _small(capacity_factor=1.0, router_bias="zipf1.1", T=200),
+    "small_f32_softmax": lambda: _small(dtype="f32", score_fn="softmax", n_group=1, topk_group=1, top_k=2,
+                                        shared_inter=0, score_bias="none", T=130),
+    "small_bf16_one_token": lambda: _small(T=1),
+    "small_bf16_gamma": lambda: _small(routed_scale=2.5, T=50, inter=384, shared_inter=128),
+    "ep8_decode_bf16_T48": lambda: workload("ep8_decode_bf16", T=48),
+    "full_decode_bf16_T40": lambda: workload("full_decode_bf16", T=40),
+}
+
+
+def _rel(a, b):
+    return O.rel_max_err(a, b)
+
+
+@pytest.mark.parametrize("name", list(LAYER_CASES))
+def test_layer_stages_match_oracle(name):
+    w = LAYER_CASES[name]()
+    say("layer case", name, {k: w[k] for k in ("T", "hidden", "n_experts", "expert_begin", "expert_end", "dtype")})
+    big = w["hidden"] >= 4096
+    run = Run(w, gen_device="cuda" if big else "cpu")
+    r = run.stages()
+    tol = TOL[w["dtype"]]
+    ref = run.oracle_forward(r["logits"])
+    # router GEMM against the oracle's fp64 logits
+    assert _rel(host(r["logits"]), ref["logits"]) < 1e-5
+    # routing and dispatch bit-exact (same logits on both sides)
+    assert np.array_equal(host(r["ids"]), ref["ids"])
+    assert np.array_equal(host(r["w"]).view(np.int32), ref["w"].view(np.int32))
+    for key in ("raw_counts", "counts", "offsets", "inv"):
+        assert np.array_equal(host(r[key]), ref[key]), key
+    R = int(ref["offsets"][-1])
+    assert np.array_equal(host(r["perm"])[:R], ref["perm"])
+    # expert rows, shared expert, layer output
+    if R:
+        assert _rel(host(r["rows"])[:R], ref["rows"]) < tol
+    if ref["shared"] is not None:
+        assert _rel(host(r["shared"]), ref["shared"]) < tol
+    err = _rel(host(r["y"]), ref["y"])
+    say("  max|dy|/rms =", err)
+    assert err < tol
+    # the fused entry point gives the same result as the stage calls
+    lo = torch.empty_like(r["logits"])
+    io = torch.empty_like(r["ids"])
+    y2 = run.forward(logits_out=lo, ids_out=io)
+    torch.cuda.synchronize()
+    assert torch.equal(lo, r["logits"]) and torch.equal(io, r["ids"])
+    assert torch.equal(y2, r["y"])
+
+
+def test_bf16_output_dtype():
+    w = _small(T=64)
+    run = Run(w, out_dtype="bf16")
+    y = run.forward()
+    run32 = Run(w, out_dtype="f32")
+    y32 = run32.forward()
+    torch.cuda.synchronize()
+    assert y.dtype == torch.bfloat16
+    assert torch.equal(y, y32.to(torch.bfloat16))
+
+
+def test_expert_parallel_shares_sum_to_whole_layer():
+    """One GPU runs the 8 EP8 shares in turn; their partial outputs, less the
+    7 extra shared-expert copies, equal the whole layer (fp32)."""
+    full = _small(dtype="f32", T=128, n_experts=64, expert_end=64)
+    EP, per = 8, 8
+    run = Run(full)
+    lo = torch.empty(full["T"], 64, dtype=torch.float32, device="cuda")
+    y_full = run.forward(logits_out=lo)
+    acc = torch.zeros_like(y_full, dtype=torch.float64)
+    for r in range(EP):
+        wr = dict(full, expert_begin=per * r, expert_end=per * r + per)
+        yr = Run(wr).forward()
+        acc += yr.double()
+    rs = Run(dict(full, expert_begin=0, expert_end=per)).stages()["shared"].double()
+    torch.cuda.synchronize()
+    d = (acc - (EP - 1) * rs - y_full.double()).abs().max().item()
+    rms = y_full.double().pow(2).mean().sqrt().item()
+    assert d / rms < 1e-5
