@@ -55,7 +55,7 @@ def stage_bytes_flops(w, counts, stage):
     if stage == "shared_gate_up":
         return (T * H + 2 * Is * H + T * Is) * eb, 2.0 * T * H * 2 * Is
     if stage == "shared_down":
-        return (T * Is + H * Is) * eb + T * H * max(eb, 2), 2.0 * T * Is * H
+        return (T * Is + H * Is) * eb + T * H * 4, 2.0 * T * Is * H
     raise ValueError(stage)
 
 

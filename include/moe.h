@@ -130,9 +130,11 @@ int moe_workspace_bytes(const moe_config* cfg, int64_t max_tokens, size_t* bytes
 /* Router GEMM: logits[T, E] (fp32) = x[T, H] . w_router[E, H]^T + router_bias.
  * x and w_router are fp32 (F32) or bf16 (BF16, FP8): inputs of the activation
  * type in, fp32 out, no separate cast (NVIDIA, "MoE layer optimisations >
- * mixed I/O RouterGEMM"). router_bias [E] fp32 may be NULL. All device. */
+ * mixed I/O RouterGEMM"). router_bias [E] fp32 may be NULL. All device; the
+ * workspace holds split-K partial sums. */
 int moe_router_gemm(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
-                    const float* router_bias, float* logits, hipStream_t stream);
+                    const float* router_bias, float* logits, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
 
 /* Scores and group-limited top-k (NVIDIA, "Top-K kernel fusion"; Perplexity,
  * "MoE Router"; glossary, "Load balancing and capacity").
@@ -174,8 +176,9 @@ int moe_dispatch(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int3
  * on the device, so no host synchronisation is needed.
  *  x          [T, H] device, activation type (bf16 for FP8)
  *  perm, offsets  from moe_dispatch
- *  out_rows   [T*k, H] device out (fp32 for F32, bf16 otherwise); rows >= R untouched
- *  shared_out [T, H] device out, same type; required iff shared_inter > 0 */
+ *  out_rows   [T*k, H] device out (fp32 for F32, bf16 otherwise: the rows are
+ *             what the combine exchange carries); rows >= R untouched
+ *  shared_out [T, H] fp32 device out; required iff shared_inter > 0 */
 int moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const int32_t* perm,
                    const int32_t* offsets, const moe_weights* weights, void* out_rows,
                    void* shared_out, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -183,7 +186,7 @@ int moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const int32_
 /* Combine (glossary step 4; infra guide section 3.1 step 4):
  *   y[t] = shared_out[t] + sum_j [inv[t,j] >= 0] * topk_w[t,j] * out_rows[inv[t,j]]
  * summed in fp32; dropped and non-local pairs add nothing (no renormalisation).
- * y [T, H] device out in cfg->out_dtype; shared_out may be NULL. */
+ * y [T, H] device out in cfg->out_dtype; shared_out [T, H] fp32 or NULL. */
 int moe_combine(const moe_config* cfg, int64_t T, const void* out_rows, const int32_t* inv,
                 const float* topk_w, const void* shared_out, void* y, hipStream_t stream);
 

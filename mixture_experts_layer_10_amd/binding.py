@@ -64,7 +64,7 @@ def lib():
             "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "moe_validate_config": (ctypes.c_int, [cfgp]),
             "moe_workspace_bytes": (ctypes.c_int, [cfgp, i64, ctypes.POINTER(ctypes.c_size_t)]),
-            "moe_router_gemm": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, vp]),
+            "moe_router_gemm": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, vp, ctypes.c_size_t, vp]),
             "moe_route": (ctypes.c_int, [cfgp, i64, fp, fp, i32p, fp, vp]),
             "moe_dispatch": (ctypes.c_int, [cfgp, i64, i32p, i32p, i32p, i32p, i32p, i32p, vp, ctypes.c_size_t, vp]),
             "moe_expert_ffn": (ctypes.c_int, [cfgp, i64, vp, i32p, i32p, wp, vp, vp, vp, ctypes.c_size_t, vp]),
@@ -210,13 +210,14 @@ def make_weights(cfg, w13, w2, shared_w13=None, shared_w2=None, w13_scale=None, 
 # Entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
 
-def moe_router_gemm(cfg, x, w_router, router_bias, logits, stream=None):
+def moe_router_gemm(cfg, x, w_router, router_bias, logits, ws, stream=None):
     T = x.shape[0]
     _check(lib().moe_router_gemm(
         ctypes.byref(cfg), T, _ptr(x, _act_dtype(cfg), (T, cfg.hidden), "x"),
         _ptr(w_router, _act_dtype(cfg), (cfg.n_experts, cfg.hidden), "w_router"),
         _ptr(router_bias, torch.float32, (cfg.n_experts,), "router_bias", optional=True),
-        _ptr(logits, torch.float32, (T, cfg.n_experts), "logits"), _stream(stream)), "moe_router_gemm")
+        _ptr(logits, torch.float32, (T, cfg.n_experts), "logits"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream)), "moe_router_gemm")
 
 
 def moe_route(cfg, logits, score_bias, topk_ids, topk_w, stream=None):
@@ -249,7 +250,7 @@ def moe_expert_ffn(cfg, x, perm, offsets, weights, out_rows, shared_out, ws, str
         ctypes.byref(cfg), T, _ptr(x, _act_dtype(cfg), (T, H), "x"), _ptr(perm, torch.int32, (T * k,), "perm"),
         _ptr(offsets, torch.int32, (cfg.n_local + 1,), "offsets"), ctypes.byref(weights),
         _ptr(out_rows, rd, (T * k, H), "out_rows"),
-        _ptr(shared_out, rd, (T, H), "shared_out", optional=cfg.shared_inter == 0),
+        _ptr(shared_out, torch.float32, (T, H), "shared_out", optional=cfg.shared_inter == 0),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream)), "moe_expert_ffn")
 
 
@@ -259,7 +260,8 @@ def moe_combine(cfg, out_rows, inv, topk_w, shared_out, y, stream=None):
     rd = _row_dtype(cfg)
     _check(lib().moe_combine(
         ctypes.byref(cfg), T, _ptr(out_rows, rd, None, "out_rows"), _ptr(inv, torch.int32, (T * k,), "inv"),
-        _ptr(topk_w, torch.float32, (T, k), "topk_w"), _ptr(shared_out, rd, (T, H), "shared_out", optional=True),
+        _ptr(topk_w, torch.float32, (T, k), "topk_w"),
+        _ptr(shared_out, torch.float32, (T, H), "shared_out", optional=True),
         _ptr(y, _out_dtype(cfg), (T, H), "y"), _stream(stream)), "moe_combine")
 
 

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
         float acc[8];
         if (a.shared) {
-            load8<ROWS_F32>(a.shared, t * H + c, acc);
+            load8<true>(a.shared, t * H + c, acc);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] = 0.0f;

@@ -37,6 +37,8 @@
 // the s-th sub-run of every lane group, identically for A and B.
 #include <float.h>
 
+#include <algorithm>
+
 #include "moe_device.h"
 
 namespace moe {
@@ -93,6 +95,8 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
     constexpr int NRF = BM / 16;                       // 16-row blocks
     constexpr int ROWS_PER_PASS = kThreads / ROWG;     // A rows loaded per pass
     constexpr int PASSES = BM / ROWS_PER_PASS;
+    constexpr int NB = PD + 1;                         // B register buffers
+    constexpr int U = (NB % 2 == 0) ? NB : 2 * NB;     // unroll: both ring indices static
     static_assert(BM % ROWS_PER_PASS == 0, "tile rows");
 
     __shared__ __attribute__((aligned(16))) unsigned char s_a[2][BM * ROWB];
@@ -100,37 +104,49 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4;
 
-    // ---- tile lookup (XCD-aware) ------------------------------------------
+    // ---- tile lookup -----------------------------------------------------
+    // Work items are (group, n-tile, m-tile, k-slice), k-slice fastest, then
+    // m-tile: the blocks that stream the same weight panel run side by side.
+    // Items are dealt to the 8 XCDs in contiguous ranges (the hardware deals
+    // blocks round-robin), so neighbouring items share an XCD's L2.
+    const int KS = a.ksplit;
     const int n_groups = a.n_local + a.has_shared;
+    const int per_item = n_tiles * KS;                 // items per m-tile
     // A null schedule means a single group of T rows.
-    const int total = (a.sched ? a.sched[n_groups] : (a.T + BM - 1) / BM) * n_tiles;
+    const int total = (a.sched ? a.sched[n_groups] : (a.T + BM - 1) / BM) * per_item;
     const int per_xcd = (total + 7) >> 3;
     const int slot = static_cast<int>(blockIdx.x >> 3);
     if (slot >= per_xcd) return;
     const int L = static_cast<int>(blockIdx.x & 7) * per_xcd + slot;
     if (L >= total) return;
-    const int mtg = L / n_tiles;
-    const int nt = L - mtg * n_tiles;
-    int lo = 0;
+    int g = 0, mt_begin = 0, mt_count = (a.T + BM - 1) / BM;
     if (a.sched) {
-        int hi = n_groups;                             // sched[lo] <= mtg < sched[hi]
+        int lo = 0, hi = n_groups;                     // sched[lo]*per_item <= L < sched[hi]*per_item
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (a.sched[mid] <= mtg) lo = mid; else hi = mid;
+            if (a.sched[mid] * per_item <= L) lo = mid; else hi = mid;
         }
+        g = lo;
+        mt_begin = a.sched[g];
+        mt_count = a.sched[g + 1] - mt_begin;
     }
-    const int g = lo;
+    const int local = L - mt_begin * per_item;
+    const int ks = local % KS;
+    const int nt = (local / KS) / mt_count;
+    const int mt = (local / KS) - nt * mt_count;
     const bool shared = a.has_shared && g == a.n_local;
     int row0 = 0, rows_g = a.T;
     if (!shared && a.offsets) {
         row0 = a.offsets[g];
         rows_g = a.offsets[g + 1] - row0;
     }
-    const int m0 = (mtg - (a.sched ? a.sched[g] : 0)) * BM;
+    const int m0 = mt * BM;
     const int rows = min(BM, rows_g - m0);
     const int nrf = (rows + 15) >> 4;
     const int K = a.K;
-    const int nch = K / T::kChunk;
+    const int nch_all = K / T::kChunk;
+    const int c_begin = (nch_all * ks) / KS;
+    const int nch = (nch_all * (ks + 1)) / KS - c_begin;
 
     // ---- B (weights): per-lane pointers of the 4 column fragments ----------
     const unsigned char* Bg = shared ? static_cast<const unsigned char*>(a.B_shared)
@@ -146,7 +162,7 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
             brow = nt * 256 + wave * 64 + 16 * f + lr;
             brow = brow < a.N ? brow : a.N - 1;        // column tail: valid row, result dropped
         }
-        bptr[f] = Bg + (static_cast<int64_t>(brow) * K) * EB + lq * RUNG * 16;
+        bptr[f] = Bg + (static_cast<int64_t>(brow) * K) * EB + lq * RUNG * 16 + static_cast<int64_t>(c_begin) * ROWB;
     }
 
     // ---- A (activations): per-thread row sources for the LDS fill ----------
@@ -162,7 +178,7 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
         if (shared) src_row = m0 + r;
         else if (a.gather) src_row = a.perm[row0 + m0 + r] / a.topk;
         else src_row = row0 + m0 + r;
-        asrc[i] = Abase + (src_row * K) * EB + aj * 16;
+        asrc[i] = Abase + (src_row * K) * EB + aj * 16 + static_cast<int64_t>(c_begin) * ROWB;
     }
     // LDS store offset (row ar, swizzled granule); pass i adds i*ROWS_PER_PASS rows.
     const int a_st = ar * ROWB + ((aj ^ (ar & (ROWG - 1))) * 16);
@@ -177,8 +193,8 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
 #pragma unroll
         for (int f = 0; f < 4; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    vec16 breg[PD + 1][4][RUNG];
-    vec16 areg[PASSES];
+    vec16 breg[NB][4][RUNG];
+    vec16 areg[2][PASSES];
 
     auto load_b = [&](vec16 (&dst)[4][RUNG], int c) {
 #pragma unroll
@@ -186,13 +202,13 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
 #pragma unroll
             for (int s = 0; s < RUNG; ++s) dst[f][s] = ld16(bptr[f] + static_cast<int64_t>(c) * ROWB + s * 16);
     };
-    auto load_a = [&](int c) {
+    auto load_a = [&](vec16 (&dst)[PASSES], int c) {
 #pragma unroll
-        for (int i = 0; i < PASSES; ++i) areg[i] = ld16(asrc[i] + static_cast<int64_t>(c) * ROWB);
+        for (int i = 0; i < PASSES; ++i) dst[i] = ld16(asrc[i] + static_cast<int64_t>(c) * ROWB);
     };
-    auto store_a = [&](int buf) {
+    auto store_a = [&](const vec16 (&src)[PASSES], int buf) {
 #pragma unroll
-        for (int i = 0; i < PASSES; ++i) st16(&s_a[buf][a_st + i * ROWS_PER_PASS * ROWB], areg[i]);
+        for (int i = 0; i < PASSES; ++i) st16(&s_a[buf][a_st + i * ROWS_PER_PASS * ROWB], src[i]);
     };
     auto compute = [&](const vec16 (&b)[4][RUNG], int buf) {
 #pragma unroll
@@ -208,23 +224,29 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
         }
     };
 
-    // ---- main loop: A one chunk ahead in LDS, B PD chunks ahead in VGPRs ----
-    load_a(0);
+    // ---- main loop ---------------------------------------------------------
+    // Chunk c's activations: global -> VGPR two iterations ahead, VGPR -> LDS
+    // at the end of iteration c-1. Chunk c's weights: global -> VGPR PD
+    // iterations ahead. Loads are issued oldest-needed first, so each wait
+    // leaves the younger loads in flight.
+    if (nch > 0) {
+        load_a(areg[0], 0);
+        if (nch > 1) load_a(areg[1], 1);
 #pragma unroll
-    for (int p = 0; p < PD; ++p)
-        if (p < nch) load_b(breg[p], p);
-    store_a(0);
-    __syncthreads();
-    for (int c0 = 0; c0 < nch; c0 += PD + 1) {
+        for (int p = 0; p < PD; ++p)
+            if (p < nch) load_b(breg[p], p);
+        store_a(areg[0], 0);
+        __syncthreads();
+    }
+    for (int c0 = 0; c0 < nch; c0 += U) {
 #pragma unroll
-        for (int u = 0; u <= PD; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int c = c0 + u;
             if (c < nch) {
-                const bool more_a = c + 1 < nch;
-                if (more_a) load_a(c + 1);
-                if (c + PD < nch) load_b(breg[(u + PD) % (PD + 1)], c + PD);
-                compute(breg[u], c & 1);
-                if (more_a) store_a((c + 1) & 1);
+                if (c + 2 < nch) load_a(areg[u & 1], c + 2);
+                if (c + PD < nch) load_b(breg[(u + PD) % NB], c + PD);
+                compute(breg[u % NB], u & 1);
+                if (c + 1 < nch) store_a(areg[(u + 1) & 1], (u + 1) & 1);
                 __syncthreads();
             }
         }
@@ -256,6 +278,8 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
             }
         }
     } else {
+        const bool split = KS > 1;
+        float* P = split ? a.partial + static_cast<int64_t>(ks) * a.T * a.ldc : nullptr;
 #pragma unroll
         for (int i = 0; i < NRF; ++i) {
             if (i < nrf) {
@@ -263,14 +287,16 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
                 for (int f = 0; f < 4; ++f) {
                     const int col = nt * 256 + wave * 64 + 16 * f + lr;
                     if (col < a.N) {
-                        const float bias = a.bias ? a.bias[col] : 0.0f;
+                        const float bias = (!split && a.bias) ? a.bias[col] : 0.0f;
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
                             const int r = i * 16 + lq * 4 + v;
                             if (r < rows) {
                                 const float o = acc[i][f][v] + bias;
                                 const int64_t off = (crow0 + r) * a.ldc + col;
-                                if (a.out_f32)
+                                if (split)
+                                    P[off] = o;
+                                else if (a.out_f32)
                                     reinterpret_cast<float*>(Cb)[off] = o;
                                 else
                                     reinterpret_cast<uint16_t*>(Cb)[off] = f32_to_bf16_bits(o);
@@ -280,6 +306,30 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
                 }
             }
         }
+    }
+}
+
+// C[t][n] = bias[n] + sum over K slices of partial[s][t][n] (fp32).
+__global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(GemmArgs a) {
+    const int64_t n = static_cast<int64_t>(a.T) * a.ldc;
+    const int64_t stride = n;
+    for (int64_t i = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4; i < n;
+         i += static_cast<int64_t>(gridDim.x) * kThreads * 4) {
+        vec16 acc = ld16(a.partial + i);
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(acc.w[j]);
+        for (int s = 1; s < a.ksplit; ++s) {
+            const vec16 p = ld16(a.partial + s * stride + i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] += __uint_as_float(p.w[j]);
+        }
+        if (a.bias) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] += a.bias[(i + j) % a.ldc];
+        }
+        st16(static_cast<float*>(a.C) + i,
+             vec16{{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])}});
     }
 }
 
@@ -310,7 +360,8 @@ void launch_one(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
 }
 
 template <Elem EL, Epi EPI>
-hipError_t launch_bm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+hipError_t launch_bm(GemmArgs a, const GemmPlan& p, hipStream_t s) {
+    a.ksplit = p.ksplit < 1 ? 1 : p.ksplit;
     switch (p.bm) {
         case 32: launch_one<EL, EPI, 32, 1>(a, p, s); break;
         case 64: launch_one<EL, EPI, 64, 1>(a, p, s); break;
@@ -328,10 +379,33 @@ GemmPlan plan_gemm(Elem e, Epi epi, int64_t rows_upper, int n_groups, int64_t ex
     p.bm = expected_rows_per_group <= 32 ? 32 : expected_rows_per_group <= 64 ? 64 : 128;
     const int cols_per_tile = epi == Epi::SWIGLU ? 128 : 256;
     p.n_tiles = (N + cols_per_tile - 1) / cols_per_tile;
+    p.ksplit = 1;
     // sum_g ceil(rows_g / bm) <= rows_upper / bm + n_groups
     const int64_t m_tiles = rows_upper / p.bm + n_groups;
     p.grid = ((m_tiles * p.n_tiles + 7) / 8) * 8;
     return p;
+}
+
+GemmPlan plan_dense_splitk(int64_t T, int N, int K, int chunk) {
+    GemmPlan p;
+    p.bm = T <= 32 ? 32 : T <= 1024 ? 64 : 128;
+    p.n_tiles = (N + 255) / 256;
+    const int64_t tiles = (T + p.bm - 1) / p.bm * p.n_tiles;
+    const int nch = K / chunk;
+    // aim for >= 512 workgroups, each slice at least 4 chunks long
+    int ks = 1;
+    while (N % 4 == 0 && ks < 16 && tiles * ks < 512 && nch / (ks * 2) >= 4) ks *= 2;
+    p.ksplit = ks;
+    p.grid = ((tiles * ks + 7) / 8) * 8;
+    return p;
+}
+
+hipError_t launch_splitk_reduce(const GemmArgs& a, int ksplit, hipStream_t s) {
+    if (ksplit <= 1) return hipSuccess;
+    const int64_t n4 = (static_cast<int64_t>(a.T) * a.ldc + 3) / 4;
+    const int64_t blocks = std::min<int64_t>((n4 + kThreads - 1) / kThreads, 4096);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_t s) {

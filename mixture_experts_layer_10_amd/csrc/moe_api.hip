@@ -51,9 +51,11 @@ Elem gemm_elem(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? Elem::F
 
 // Workspace layout for up to T tokens; every region 256-byte aligned.
 struct Layout {
-    size_t logits, ids, w, raw, counts, offsets, perm, inv, chunk_hist, chunk_base, sched;
+    size_t logits, ids, w, raw, counts, offsets, perm, inv, chunk_hist, chunk_base, sched, partial;
     size_t h, h_shared, rows, shared_out, total;
 };
+
+int router_chunk(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 64 : 128; }
 
 Layout layout(const moe_config* c, int64_t T) {
     const int64_t E = c->n_experts, El = c->expert_end - c->expert_begin, k = c->top_k;
@@ -77,10 +79,12 @@ Layout layout(const moe_config* c, int64_t T) {
     L.chunk_hist = take(sizeof(int32_t) * nchunk * El);
     L.chunk_base = take(sizeof(int32_t) * nchunk * El);
     L.sched = take(sizeof(int32_t) * (El + 2));
+    const GemmPlan rp = plan_dense_splitk(T, c->n_experts, c->hidden, router_chunk(c));
+    L.partial = take(rp.ksplit > 1 ? sizeof(float) * rp.ksplit * T * E : 0);
     L.h = take(static_cast<size_t>(act_bytes(c)) * P * c->inter);
     L.h_shared = take(static_cast<size_t>(act_bytes(c)) * T * c->shared_inter);
     L.rows = take(static_cast<size_t>(row_bytes(c)) * P * c->hidden);
-    L.shared_out = take(static_cast<size_t>(row_bytes(c)) * T * c->hidden);
+    L.shared_out = take(sizeof(float) * T * c->hidden);
     L.total = off;
     return L;
 }
@@ -136,8 +140,9 @@ int64_t capacity_of(const moe_config* c, int64_t T) {
 // ---- stage bodies (arguments already validated) ------------------------------
 
 hipError_t do_router_gemm(const moe_config* c, int64_t T, const void* x, const void* wr, const float* bias,
-                          float* logits, hipStream_t s) {
+                          float* logits, void* ws, hipStream_t s) {
     StageTimer tm(MOE_STAGE_ROUTER_GEMM, s);
+    const Layout L = layout(c, T);
     GemmArgs g{};
     g.A = g.A_shared = x;
     g.B = g.B_shared = wr;
@@ -149,8 +154,12 @@ hipError_t do_router_gemm(const moe_config* c, int64_t T, const void* x, const v
     g.ldc = c->n_experts;
     g.bias = bias;
     g.out_f32 = 1;
-    const GemmPlan p = plan_gemm(gemm_elem(c), Epi::PLAIN, T, 1, T, c->n_experts);
-    return launch_gemm(gemm_elem(c), Epi::PLAIN, g, p, s);
+    const GemmPlan p = plan_dense_splitk(T, c->n_experts, c->hidden, router_chunk(c));
+    g.ksplit = p.ksplit;
+    g.partial = at<float>(ws, L.partial);
+    hipError_t e = launch_gemm(gemm_elem(c), Epi::PLAIN, g, p, s);
+    if (e == hipSuccess) e = launch_splitk_reduce(g, p.ksplit, s);
+    return e;
 }
 
 hipError_t do_route(const moe_config* c, int64_t T, const float* logits, const float* sbias, int32_t* ids,
@@ -275,7 +284,7 @@ hipError_t do_expert_ffn(const moe_config* c, int64_t T, const void* x, const in
         s2.inter = 0;
         s2.C = s2.C_shared = shared_out;
         s2.ldc = static_cast<int>(H);
-        s2.out_f32 = c->dtype == MOE_DTYPE_F32;
+        s2.out_f32 = 1;          // the shared output stays fp32 (it is never exchanged)
         const GemmPlan q2 = plan_gemm(el, Epi::PLAIN, T, 1, T, static_cast<int>(H));
         StageTimer tm(MOE_STAGE_SHARED_DOWN, s);
         if ((e = launch_gemm(el, Epi::PLAIN, s2, q2, s)) != hipSuccess) return e;
@@ -290,7 +299,7 @@ hipError_t do_combine(const moe_config* c, int64_t T, const void* rows, const in
     a.rows = rows;
     a.inv = inv;
     a.w = w;
-    a.shared = shared_out;
+    a.shared = static_cast<const float*>(shared_out);
     a.y = y;
     a.T = T;
     a.H = c->hidden;
@@ -339,14 +348,15 @@ int moe_workspace_bytes(const moe_config* cfg, int64_t max_tokens, size_t* bytes
 }
 
 int moe_router_gemm(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* router_bias,
-                    float* logits, hipStream_t stream) {
+                    float* logits, void* ws, size_t ws_bytes, hipStream_t stream) {
     int st = validate(cfg);
     if (st) return st;
     if (T < 0 || T > INT32_MAX / 16) return MOE_ERR_INVALID_ARG;
     if (T == 0) return MOE_OK;
     if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits)) return MOE_ERR_MISALIGNED;
-    return hip_status(do_router_gemm(cfg, T, x, w_router, router_bias, logits, stream));
+    if ((st = check_ws(cfg, T, ws, ws_bytes))) return st;
+    return hip_status(do_router_gemm(cfg, T, x, w_router, router_bias, logits, ws, stream));
 }
 
 int moe_route(const moe_config* cfg, int64_t T, const float* logits, const float* score_bias, int32_t* topk_ids,
@@ -425,7 +435,7 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
     void* rows = at<void>(ws, L.rows);
     void* shared_out = cfg->shared_inter > 0 ? at<void>(ws, L.shared_out) : nullptr;
     hipError_t e;
-    if ((e = do_router_gemm(cfg, T, x, w_router, router_bias, logits, stream)) != hipSuccess) return MOE_ERR_HIP;
+    if ((e = do_router_gemm(cfg, T, x, w_router, router_bias, logits, ws, stream)) != hipSuccess) return MOE_ERR_HIP;
     if ((e = do_route(cfg, T, logits, score_bias, ids, w, stream)) != hipSuccess) return MOE_ERR_HIP;
     if ((e = do_dispatch(cfg, T, ids, at<int32_t>(ws, L.raw), at<int32_t>(ws, L.counts), offsets, perm, inv, ws,
                          stream)) != hipSuccess)

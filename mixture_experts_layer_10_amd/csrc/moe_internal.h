@@ -77,16 +77,27 @@ struct GemmArgs {
     int ldc;
     const float* bias;        // PLAIN fp32 out: per-column bias or null
     int out_f32;              // PLAIN: 1 -> fp32 output, 0 -> bf16 output
+    // Split-K (PLAIN, fp32 output, single group only): K-slice s of tile t
+    // writes fp32 partial sums to partial[s][row][col]; a reduce kernel adds
+    // the slices and the bias into C.
+    int ksplit;               // >= 1
+    float* partial;           // [ksplit, T, ldc] when ksplit > 1
 };
 
 struct GemmPlan {
     int bm;                   // rows per tile
     int n_tiles;              // column tiles per group
-    int64_t grid;             // workgroups launched (upper bound on tiles)
+    int ksplit;               // K slices per tile
+    int64_t grid;             // workgroups launched (upper bound on tiles * ksplit)
 };
 GemmPlan plan_gemm(Elem e, Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N);
 hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_t s);
 hipError_t launch_gemm(Elem e, Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
+// Dense (single-group) PLAIN GEMM with fp32 output, split along K when the
+// tile grid alone would leave the GPU idle; `partial` must hold
+// max_split * T * N floats.
+GemmPlan plan_dense_splitk(int64_t T, int N, int K, int chunk);
+hipError_t launch_splitk_reduce(const GemmArgs& a, int ksplit, hipStream_t s);
 
 // --- activation quantisation (K4) -------------------------------------------
 hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* q, float* scale, int64_t rows, int cols, hipStream_t s);
@@ -96,11 +107,11 @@ struct CombineArgs {
     const void* rows;         // [R, H]
     const int32_t* inv;       // [T, k]
     const float* w;           // [T, k]
-    const void* shared;       // [T, H] or null
+    const float* shared;      // [T, H] fp32 or null
     void* y;                  // [T, H]
     int64_t T;
     int H, k;
-    int rows_f32;             // rows/shared are fp32 (else bf16)
+    int rows_f32;             // rows are fp32 (else bf16)
     int out_f32;              // y is fp32 (else bf16)
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

@@ -34,9 +34,10 @@ Routing decisions (an argmax over floating-point scores) are taken in float32
 with the recipe below, step for step, so that the GPU can match them bit for
 bit. Between stages the oracle rounds to the carrier type the layer uses: the
 intermediate activation h to the activation type (bf16 round-to-nearest-even,
-or e4m3 with 1x128 scales), and each expert output row and the shared output
-to bf16 when activations are bf16 or fp8 (the combine exchange carries BF16,
-infra guide section 3.2).
+or e4m3 with 1x128 scales), and each routed expert's output row to bf16 when
+activations are bf16 or fp8 (the combine exchange carries BF16, infra guide
+section 3.2). The shared expert's output never leaves the token's GPU and is
+kept unrounded.
 
 Readings where the pages are silent (each also listed in the design doc):
   * group score = sum of the two largest selection scores in the group;
@@ -368,14 +369,15 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def swiglu_expert(cfg, x_rows, w13, w2, inter, w13_scale=None, w2_scale=None):
+def swiglu_expert(cfg, x_rows, w13, w2, inter, w13_scale=None, w2_scale=None, round_out=True):
     """o = (silu(x W_g^T) * (x W_u^T)) W_d^T for the given rows.
 
     x_rows: [n, H] input rows (their exact stored values). w13: [2I, H] with
     rows 0..I-1 the gate and I..2I-1 the up projection; w2: [H, I]. For fp8
     the weights are e4m3 codes with 128x128 block scales and the activations
-    are quantised per 1x128 block before each GEMM. Returns fp64 [n, H],
-    rounded to the carrier type of the expert output.
+    are quantised per 1x128 block before each GEMM. Returns fp64 [n, H]; with
+    round_out (routed experts, whose outputs travel through the combine) the
+    rows are rounded to their bf16 carrier when activations are bf16 or fp8.
     """
     if cfg.act == "fp8":
         W13 = dequant_block_weight(w13, w13_scale)
@@ -395,7 +397,7 @@ def swiglu_expert(cfg, x_rows, w13, w2, inter, w13_scale=None, w2_scale=None):
     else:
         ha = _round_act(h, cfg.act)
     o = ha @ W2.T
-    if cfg.act in ("bf16", "fp8"):
+    if round_out and cfg.act in ("bf16", "fp8"):
         o = bf16_round(o)
     return o
 
@@ -443,7 +445,8 @@ def experts_forward(cfg, x, disp, w13, w2, w13_scale=None, w2_scale=None):
 def shared_forward(cfg, x, sw13, sw2, sw13_scale=None, sw2_scale=None):
     if cfg.shared_inter <= 0:
         return None
-    return swiglu_expert(cfg, x, sw13, sw2, cfg.shared_inter, sw13_scale, sw2_scale)
+    # The shared expert's output stays on the token's own GPU: no bf16 carrier.
+    return swiglu_expert(cfg, x, sw13, sw2, cfg.shared_inter, sw13_scale, sw2_scale, round_out=False)
 
 
 def forward(cfg, x, w_router, w13, w2, router_bias=None, score_bias=None,
@@ -480,7 +483,8 @@ def forward_tokens(cfg, tokens, x_rows, ids, w, inv, get_expert, shared_w=None):
     n = len(tokens)
     y = np.zeros((n, cfg.hidden), dtype=np.float64)
     if shared_w is not None:
-        y += swiglu_expert(cfg, x_rows, shared_w[0], shared_w[1], cfg.shared_inter, shared_w[2], shared_w[3])
+        y += swiglu_expert(cfg, x_rows, shared_w[0], shared_w[1], cfg.shared_inter, shared_w[2], shared_w[3],
+                           round_out=False)
     need = {}
     for i, t in enumerate(tokens):
         for j in range(k):

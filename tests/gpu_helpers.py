@@ -51,7 +51,7 @@ class Run:
         dev = "cuda"
         r = {}
         r["logits"] = torch.empty(T, E, dtype=torch.float32, device=dev)
-        moe.moe_router_gemm(c, i["x"], i["w_router"], i["router_bias"], r["logits"])
+        moe.moe_router_gemm(c, i["x"], i["w_router"], i["router_bias"], r["logits"], self.ws)
         r["ids"] = torch.empty(T, k, dtype=torch.int32, device=dev)
         r["w"] = torch.empty(T, k, dtype=torch.float32, device=dev)
         moe.moe_route(c, r["logits"], i["score_bias"], r["ids"], r["w"])
@@ -63,7 +63,7 @@ class Run:
         moe.moe_dispatch(c, r["ids"], r["raw_counts"], r["counts"], r["offsets"], r["perm"], r["inv"], self.ws)
         rd = torch.float32 if c.dtype == moe.DTYPE_F32 else torch.bfloat16
         r["rows"] = torch.zeros(T * k, H, dtype=rd, device=dev)
-        r["shared"] = torch.zeros(T, H, dtype=rd, device=dev) if c.shared_inter else None
+        r["shared"] = torch.zeros(T, H, dtype=torch.float32, device=dev) if c.shared_inter else None
         moe.moe_expert_ffn(c, i["x"], r["perm"], r["offsets"], self.W, r["rows"], r["shared"], self.ws)
         od = torch.float32 if c.out_dtype == moe.DTYPE_F32 else torch.bfloat16
         r["y"] = torch.empty(T, H, dtype=od, device=dev)

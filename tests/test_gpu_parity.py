@@ -202,7 +202,12 @@ def test_layer_stages_match_oracle(name):
     assert np.array_equal(host(r["perm"])[:R], ref["perm"])
     # expert rows, shared expert, layer output
     if R:
-        assert _rel(host(r["rows"])[:R], ref["rows"]) < tol
+        # both sides round each expert row to its bf16 carrier: allow the one
+        # bf16 step a rounding-boundary straddle gives (2**-7 relative, at most)
+        got, want = host(r["rows"])[:R].astype(np.float64), ref["rows"]
+        slack = 2.0 ** -7 * np.abs(want) if w["dtype"] != "f32" else 0.0
+        rms = math.sqrt(float(np.mean(want * want)))
+        assert float(np.max(np.maximum(np.abs(got - want) - slack, 0.0))) / rms < tol
     if ref["shared"] is not None:
         assert _rel(host(r["shared"]), ref["shared"]) < tol
     err = _rel(host(r["y"]), ref["y"])

@@ -119,4 +119,4 @@ def test_binding_requires_gpu_tensors():
     c = moe.make_config(512, 8, 2, 512, dtype="f32")
     x = torch.zeros(4, 512)
     with pytest.raises(ValueError):
-        moe.moe_router_gemm(c, x, torch.zeros(8, 512), None, torch.zeros(4, 8))
+        moe.moe_router_gemm(c, x, torch.zeros(8, 512), None, torch.zeros(4, 8), torch.zeros(16, dtype=torch.uint8))
