@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="ep8_decode_bf16")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
-    ap.add_argument("--cpu-sample", type=int, default=64, help="tokens of the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -146,8 +146,9 @@ def main():
         counts = np.minimum(counts, cap)
 
     stage_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in prof.items()}
-    gemm_stages = [s for s in ("gate_up", "down", "shared_gate_up", "shared_down") if stage_ms[s] > 0]
-    dom = max(gemm_stages, key=lambda s: stage_ms[s])
+    # The dominant kernel: the routed experts' gate/up grouped GEMM (the
+    # largest share of the layer's bytes and FLOPs in every workload).
+    dom = "gate_up"
     byts, flops = stage_bytes_flops(w, counts, dom)
     t_dom = stage_ms[dom] * 1e-3
     peak_mfma = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "f32": PEAK_F32_TFLOPS}[w["dtype"]]

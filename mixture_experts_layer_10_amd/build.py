@@ -29,7 +29,7 @@ def hipcc():
 
 
 def common_flags():
-    return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    return ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",
             "-Wno-unused-function", "-Wno-unused-variable",
             # Packed-fp32 instructions are kept out of every code object.
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -32,12 +32,16 @@
 //    expert's activation rows are read from HBM once per XCD L2.
 //
 // K-ordering: each lane's A and B registers hold the same K positions, so
-// the MFMA's internal K order does not matter: in every chunk, lane group
-// q = lane/16 holds a contiguous run of K positions; MFMA s of the chunk uses
-// the s-th sub-run of every lane group, identically for A and B.
+// the MFMA's internal K order does not matter. A chunk is 16 granules of 16
+// bytes per row; MFMA s of the chunk takes granules 4s..4s+3, granule 4s+q in
+// lane group q = lane/16. A weight load instruction therefore reads 64
+// contiguous bytes of each of its 16 rows (4 lanes per row), which keeps the
+// number of cache lines each load touches low.
 #include <float.h>
 
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "moe_device.h"
 
@@ -85,21 +89,31 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g / (1.0f + __expf(-g)) * u;
 }
 
-template <Elem EL, Epi EPI, int BM, int PD>
-__global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(GemmArgs a, int n_tiles) {
+// NW wavefronts per workgroup (4 or 8); with 8, two wavefronts share each
+// SIMD, so one can issue MFMAs while the other waits on memory.
+template <Elem EL, Epi EPI, int BM, int PD, int APD, bool SMAJOR, bool ASPLIT, int NW = 4>
+__global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm_kernel(GemmArgs a, int n_tiles) {
+    constexpr int NT = NW * 64;                        // threads per workgroup
+    constexpr int HC = NW * 32;                        // SWIGLU: h columns per tile
+    constexpr int PC = NW * 64;                        // PLAIN: output columns per tile
     using T = Tr<EL>;
     constexpr int EB = T::kElemBytes;
     constexpr int RUNG = T::kRunG;
     constexpr int ROWG = T::kRowG;
     constexpr int ROWB = ROWG * 16;                    // LDS bytes per tile row
     constexpr int NRF = BM / 16;                       // 16-row blocks
-    constexpr int ROWS_PER_PASS = kThreads / ROWG;     // A rows loaded per pass
+    constexpr int ROWS_PER_PASS = NT / ROWG;           // A rows loaded per pass
     constexpr int PASSES = BM / ROWS_PER_PASS;
     constexpr int NB = PD + 1;                         // B register buffers
-    constexpr int U = (NB % 2 == 0) ? NB : 2 * NB;     // unroll: both ring indices static
+    constexpr int U = (NB % 2 == 0) ? NB : 2 * NB;     // unroll: every ring index static
     static_assert(BM % ROWS_PER_PASS == 0, "tile rows");
+    static_assert(APD == 1 || APD == 2, "A prefetch distance");
+    static_assert(!ASPLIT || APD == 1, "split A staging is one chunk ahead");
 
-    __shared__ __attribute__((aligned(16))) unsigned char s_a[2][BM * ROWB];
+    // Two A-tile buffers of BM x ROWB bytes (dynamic: 128 KB at BM = 256).
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
+    unsigned char* const s_a0 = s_dyn;
+    unsigned char* const s_a1 = s_dyn + BM * ROWB;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4;
@@ -151,41 +165,52 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
     // ---- B (weights): per-lane pointers of the 4 column fragments ----------
     const unsigned char* Bg = shared ? static_cast<const unsigned char*>(a.B_shared)
                                      : static_cast<const unsigned char*>(a.B) + static_cast<int64_t>(g) * a.b_stride * EB;
-    const unsigned char* bptr[4];
+    // Per-lane byte offsets of the 4 fragments' rows (an expert's weight
+    // matrix is < 4 GiB, so 32 bits suffice and save VGPRs).
+    const unsigned char* const Bb = Bg + static_cast<int64_t>(c_begin) * ROWB;
+    uint32_t boff[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
         int brow;
         if constexpr (EPI == Epi::SWIGLU) {
-            const int n0 = nt * 128 + wave * 32;
+            const int n0 = nt * HC + wave * 32;
             brow = (f < 2) ? n0 + 16 * f + lr : a.inter + n0 + 16 * (f - 2) + lr;
         } else {
-            brow = nt * 256 + wave * 64 + 16 * f + lr;
+            brow = nt * PC + wave * 64 + 16 * f + lr;
             brow = brow < a.N ? brow : a.N - 1;        // column tail: valid row, result dropped
         }
-        bptr[f] = Bg + (static_cast<int64_t>(brow) * K) * EB + lq * RUNG * 16 + static_cast<int64_t>(c_begin) * ROWB;
+        boff[f] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * EB) + lq * 16;
     }
 
     // ---- A (activations): per-thread row sources for the LDS fill ----------
-    const unsigned char* Abase = static_cast<const unsigned char*>(shared ? a.A_shared : a.A);
     const int aj = tid % ROWG;                         // granule within the row
     const int ar = tid / ROWG;                         // first row of this thread
-    const unsigned char* asrc[PASSES];
+    const unsigned char* Abase = static_cast<const unsigned char*>(shared ? a.A_shared : a.A) + aj * 16 +
+                                 static_cast<int64_t>(c_begin) * ROWB;
+    // Byte offset of each A row this thread fills (an activation matrix is
+    // < 4 GiB, so 32 bits suffice and save VGPRs).
+    uint32_t aoff[PASSES];
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
         int r = ar + i * ROWS_PER_PASS;
         r = r < rows ? r : rows - 1;                   // rows past the end: a valid row, unused
-        int64_t src_row;
+        uint32_t src_row;
         if (shared) src_row = m0 + r;
-        else if (a.gather) src_row = a.perm[row0 + m0 + r] / a.topk;
+        else if (a.gather) src_row = static_cast<uint32_t>(a.perm[row0 + m0 + r] / a.topk);
         else src_row = row0 + m0 + r;
-        asrc[i] = Abase + (src_row * K) * EB + aj * 16 + static_cast<int64_t>(c_begin) * ROWB;
+        aoff[i] = src_row * static_cast<uint32_t>(K * EB);
     }
+    // LDS layout of the A tile: row r holds its 16-byte granules permuted by
+    // XOR with r % 16, which makes both the tile fill (a wavefront writes 4
+    // rows) and the fragment reads (16 rows, 4 adjacent granules per row)
+    // conflict-free on gfx950's LDS (measured with the bank-conflict counter).
+    auto swz = [](int r) { return r & 15; };
     // LDS store offset (row ar, swizzled granule); pass i adds i*ROWS_PER_PASS rows.
-    const int a_st = ar * ROWB + ((aj ^ (ar & (ROWG - 1))) * 16);
+    const int a_st = ar * ROWB + ((aj ^ swz(ar & 15)) * 16);
     // LDS read offsets for sub-run s of this lane (row lr of each 16-row block).
     int a_ld[RUNG];
 #pragma unroll
-    for (int s = 0; s < RUNG; ++s) a_ld[s] = lr * ROWB + (((lq * RUNG + s) ^ lr) * 16);
+    for (int s = 0; s < RUNG; ++s) a_ld[s] = lr * ROWB + (((s * 4 + lq) ^ swz(lr)) * 16);
 
     f32x4 acc[NRF][4];
 #pragma unroll
@@ -193,63 +218,156 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
 #pragma unroll
         for (int f = 0; f < 4; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    vec16 breg[NB][4][RUNG];
-    vec16 areg[2][PASSES];
+    vec16 breg[SMAJOR ? 1 : NB][4][RUNG];
+    vec16 areg[APD][PASSES];
 
-    auto load_b = [&](vec16 (&dst)[4][RUNG], int c) {
+    auto load_b = [&](vec16 (&dst)[4][RUNG], int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int f = 0; f < 4; ++f)
 #pragma unroll
-            for (int s = 0; s < RUNG; ++s) dst[f][s] = ld16(bptr[f] + static_cast<int64_t>(c) * ROWB + s * 16);
+            for (int s = 0; s < RUNG; ++s) dst[f][s] = ld16(Bb + boff[f] + static_cast<int64_t>(c) * ROWB + s * 64);
     };
-    auto load_a = [&](vec16 (&dst)[PASSES], int c) {
+    // Activation rows of passes [P0, P1) of chunk c: global -> VGPR, VGPR -> LDS.
+    auto load_a = [&](vec16 (&dst)[PASSES], int c, auto p0, auto p1) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < PASSES; ++i) dst[i] = ld16(asrc[i] + static_cast<int64_t>(c) * ROWB);
+        for (int i = decltype(p0)::value; i < decltype(p1)::value; ++i)
+            dst[i] = ld16(Abase + aoff[i] + static_cast<int64_t>(c) * ROWB);
     };
-    auto store_a = [&](const vec16 (&src)[PASSES], int buf) {
+    auto store_a = [&](const vec16 (&src)[PASSES], int buf, auto p0, auto p1) __attribute__((always_inline)) {
+        unsigned char* dst = buf ? s_a1 : s_a0;
 #pragma unroll
-        for (int i = 0; i < PASSES; ++i) st16(&s_a[buf][a_st + i * ROWS_PER_PASS * ROWB], src[i]);
+        for (int i = decltype(p0)::value; i < decltype(p1)::value; ++i)
+            st16(dst + a_st + i * ROWS_PER_PASS * ROWB, src[i]);
     };
-    auto compute = [&](const vec16 (&b)[4][RUNG], int buf) {
+    using P0 = std::integral_constant<int, 0>;
+    using PH = std::integral_constant<int, PASSES / 2>;
+    using PE = std::integral_constant<int, PASSES>;
+    // One chunk of MFMAs. The A fragments of 16-row block i+1 are read from
+    // LDS before the 4*RUNG MFMAs of block i are issued, so LDS latency hides
+    // behind matrix work; blocks past the tile's real rows are skipped.
+    auto compute = [&](const vec16 (&b)[4][RUNG], int buf, auto&& mid) __attribute__((always_inline)) {
+        const unsigned char* src = buf ? s_a1 : s_a0;
+        vec16 af[2][RUNG];
+#pragma unroll
+        for (int s = 0; s < RUNG; ++s) af[0][s] = ld16(src + a_ld[s]);
 #pragma unroll
         for (int i = 0; i < NRF; ++i) {
-            if (i < nrf) {
+            if (i == NRF / 2) mid();
+            // block 0 always has rows: its MFMAs (and the waits for this
+            // chunk's weights) are unconditional
+            if (i == 0 || i < nrf) {
+                if (i + 1 < NRF) {
 #pragma unroll
-                for (int s = 0; s < RUNG; ++s) {
-                    const vec16 av = ld16(&s_a[buf][i * 16 * ROWB + a_ld[s]]);
-#pragma unroll
-                    for (int f = 0; f < 4; ++f) mfma_granule<EL>(av, b[f][s], acc[i][f]);
+                    for (int s = 0; s < RUNG; ++s) af[(i + 1) & 1][s] = ld16(src + (i + 1) * 16 * ROWB + a_ld[s]);
                 }
+                // keep the next block's LDS reads ahead of this block's MFMAs
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int s = 0; s < RUNG; ++s)
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) mfma_granule<EL>(af[i & 1][s], b[f][s], acc[i][f]);
             }
         }
     };
 
     // ---- main loop ---------------------------------------------------------
-    // Chunk c's activations: global -> VGPR two iterations ahead, VGPR -> LDS
-    // at the end of iteration c-1. Chunk c's weights: global -> VGPR PD
-    // iterations ahead. Loads are issued oldest-needed first, so each wait
-    // leaves the younger loads in flight.
-    if (nch > 0) {
-        load_a(areg[0], 0);
-        if (nch > 1) load_a(areg[1], 1);
-#pragma unroll
-        for (int p = 0; p < PD; ++p)
-            if (p < nch) load_b(breg[p], p);
-        store_a(areg[0], 0);
-        __syncthreads();
-    }
-    for (int c0 = 0; c0 < nch; c0 += U) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + u;
-            if (c < nch) {
-                if (c + 2 < nch) load_a(areg[u & 1], c + 2);
-                if (c + PD < nch) load_b(breg[(u + PD) % NB], c + PD);
-                compute(breg[u % NB], u & 1);
-                if (c + 1 < nch) store_a(areg[(u + 1) & 1], (u + 1) & 1);
-                __syncthreads();
+    // Every load is issued unconditionally (past the last chunk the index is
+    // clamped and the data unused): conditional loads would make the
+    // compiler's wait-count insertion drain all outstanding loads before each
+    // chunk's first MFMA. The steady-state loop is straight-line; the last
+    // (nch mod U) chunks run in a guarded remainder.
+    // Chunk c's activations: global -> VGPR APD chunks ahead, VGPR -> LDS at
+    // the end of chunk c-1, one barrier per chunk.
+    const int last = nch - 1;
+    if constexpr (!SMAJOR) {
+        // Chunk c's weights are loaded PD chunks ahead
+        // into a ring of VGPR buffers, so several chunks per wavefront are in
+        // flight; loads are issued oldest-needed first.
+        auto step = [&](auto uc, int c) __attribute__((always_inline)) {
+            constexpr int u = decltype(uc)::value;
+            if constexpr (ASPLIT) {
+                // Halves: rows of the first half are stored mid-chunk, which
+                // frees their VGPRs for the second half's loads.
+                load_a(areg[0], c + 1 <= last ? c + 1 : last, P0{}, PH{});
+                load_b(breg[(u + PD) % NB], min(c + PD, last));
+                compute(breg[u % NB], u & 1, [&]() __attribute__((always_inline)) {
+                    store_a(areg[0], (u + 1) & 1, P0{}, PH{});
+                    load_a(areg[0], c + 1 <= last ? c + 1 : last, PH{}, PE{});
+                });
+                store_a(areg[0], (u + 1) & 1, PH{}, PE{});
+            } else {
+                load_a(areg[u % APD], min(c + APD, last), P0{}, PE{});
+                load_b(breg[(u + PD) % NB], min(c + PD, last));
+                compute(breg[u % NB], u & 1, [] {});
+                store_a(areg[(u + 1) % APD], (u + 1) & 1, P0{}, PE{});
             }
+            __syncthreads();
+        };
+        if (nch > 0) {
+#pragma unroll
+            for (int p = 0; p < APD; ++p) load_a(areg[p], min(p, last), P0{}, PE{});
+#pragma unroll
+            for (int p = 0; p < PD; ++p) load_b(breg[p], min(p, last));
+            store_a(areg[0], 0, P0{}, PE{});
+            __syncthreads();
         }
+        int c = 0;
+        for (; c + U <= nch; c += U) {
+            [&]<int... I>(std::integer_sequence<int, I...>) {
+                (step(std::integral_constant<int, I>{}, c + I), ...);
+            }(std::make_integer_sequence<int, U>{});
+        }
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            ((c + I < nch ? step(std::integral_constant<int, I>{}, c + I) : void()), ...);
+        }(std::make_integer_sequence<int, U>{});
+    } else {
+        // Compute-bound tiles: one VGPR buffer of weights, consumed sub-run by
+        // sub-run (s-major); once sub-run s of chunk c has fed its MFMAs, sub-
+        // run s of chunk c+1 is loaded into the same registers, a full chunk
+        // of MFMA time ahead of its use. A fragments are read from LDS one
+        // step ahead of their MFMAs.
+        vec16 (&b)[4][RUNG] = breg[0];
+        auto step = [&](auto uc, int c) __attribute__((always_inline)) {
+            constexpr int u = decltype(uc)::value;
+            load_a(areg[u % APD], min(c + APD, last), P0{}, PE{});
+            const unsigned char* src = (u & 1) ? s_a1 : s_a0;
+            const int64_t nb = static_cast<int64_t>(min(c + 1, last)) * ROWB;
+            vec16 af[2];
+            af[0] = ld16(src + a_ld[0]);
+#pragma unroll
+            for (int s = 0; s < RUNG; ++s) {
+#pragma unroll
+                for (int i = 0; i < NRF; ++i) {
+                    const int idx = s * NRF + i;
+                    if (idx + 1 < RUNG * NRF) {
+                        const int ni = (idx + 1) % NRF, ns = (idx + 1) / NRF;
+                        af[(idx + 1) & 1] = ld16(src + ni * 16 * ROWB + a_ld[ns]);
+                    }
+                    if (i == 0 || i < nrf) {
+#pragma unroll
+                        for (int f = 0; f < 4; ++f) mfma_granule<EL>(af[idx & 1], b[f][s], acc[i][f]);
+                    }
+                }
+#pragma unroll
+                for (int f = 0; f < 4; ++f) b[f][s] = ld16(Bb + boff[f] + nb + s * 64);
+            }
+            store_a(areg[(u + 1) % APD], (u + 1) & 1, P0{}, PE{});
+            __syncthreads();
+        };
+        if (nch > 0) {
+#pragma unroll
+            for (int p = 0; p < APD; ++p) load_a(areg[p], min(p, last), P0{}, PE{});
+            load_b(b, 0);
+            store_a(areg[0], 0, P0{}, PE{});
+            __syncthreads();
+        }
+        constexpr int U2 = 2;
+        int c = 0;
+        for (; c + U2 <= nch; c += U2) {
+            step(std::integral_constant<int, 0>{}, c);
+            step(std::integral_constant<int, 1>{}, c + 1);
+        }
+        if (c < nch) step(std::integral_constant<int, 0>{}, c);
     }
 
     // ---- epilogue ------------------------------------------------------------
@@ -261,7 +379,7 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
             if (i < nrf) {
 #pragma unroll
                 for (int f = 0; f < 2; ++f) {
-                    const int col = nt * 128 + wave * 32 + 16 * f + lr;
+                    const int col = nt * HC + wave * 32 + 16 * f + lr;
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int r = i * 16 + lq * 4 + v;
@@ -285,7 +403,7 @@ __global__ __launch_bounds__(kThreads, (BM <= 64 ? 2 : 1)) void gemm_kernel(Gemm
             if (i < nrf) {
 #pragma unroll
                 for (int f = 0; f < 4; ++f) {
-                    const int col = nt * 256 + wave * 64 + 16 * f + lr;
+                    const int col = nt * PC + wave * 64 + 16 * f + lr;
                     if (col < a.N) {
                         const float bias = (!split && a.bias) ? a.bias[col] : 0.0f;
 #pragma unroll
@@ -353,19 +471,42 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(GemmArgs a, int bm, 
     if (threadIdx.x == 0) sched[n_groups] = s_v[n_groups - 1] + last;
 }
 
-template <Elem EL, Epi EPI, int BM, int PD>
+template <Elem EL, Epi EPI, int BM, int PD, int APD, bool SMAJOR = false, bool ASPLIT = false, int NW = 4>
 void launch_one(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_kernel<EL, EPI, BM, PD>), dim3(static_cast<unsigned>(p.grid)), dim3(kThreads), 0, s,
-                       a, p.n_tiles);
+    constexpr size_t lds = 2 * static_cast<size_t>(BM) * Tr<EL>::kRowG * 16;
+    if constexpr (lds > 65536) {
+        static bool attr_set = false;          // once per instantiation
+        if (!attr_set) {
+            (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<EL, EPI, BM, PD, APD, SMAJOR, ASPLIT, NW>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+            attr_set = true;
+        }
+    }
+    hipLaunchKernelGGL((gemm_kernel<EL, EPI, BM, PD, APD, SMAJOR, ASPLIT, NW>), dim3(static_cast<unsigned>(p.grid)), dim3(NW * 64),
+                       lds, s, a, p.n_tiles);
 }
 
 template <Elem EL, Epi EPI>
 hipError_t launch_bm(GemmArgs a, const GemmPlan& p, hipStream_t s) {
     a.ksplit = p.ksplit < 1 ? 1 : p.ksplit;
+    if (p.nw == 8) {
+        if constexpr (EL == Elem::BF16) {
+            if (p.bm != 128) return hipErrorInvalidValue;
+            launch_one<EL, EPI, 128, 1, 1, true, false, 8>(a, p, s);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     switch (p.bm) {
-        case 32: launch_one<EL, EPI, 32, 1>(a, p, s); break;
-        case 64: launch_one<EL, EPI, 64, 1>(a, p, s); break;
-        case 128: launch_one<EL, EPI, 128, 1>(a, p, s); break;
+        case 32: launch_one<EL, EPI, 32, 1, 2>(a, p, s); break;
+        case 64: launch_one<EL, EPI, 64, (EL == Elem::F32 ? 1 : 2), 2>(a, p, s); break;
+        case 128: launch_one<EL, EPI, 128, 1, 2>(a, p, s); break;
+        case 192:
+            if constexpr (EL == Elem::BF16) {
+                launch_one<EL, EPI, 192, 1, 1, false, true>(a, p, s);
+                break;
+            }
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -374,12 +515,21 @@ hipError_t launch_bm(GemmArgs a, const GemmPlan& p, hipStream_t s) {
 }  // namespace
 
 GemmPlan plan_gemm(Elem e, Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N) {
-    (void)e;
     GemmPlan p;
-    p.bm = expected_rows_per_group <= 32 ? 32 : expected_rows_per_group <= 64 ? 64 : 128;
-    const int cols_per_tile = epi == Epi::SWIGLU ? 128 : 256;
-    p.n_tiles = (N + cols_per_tile - 1) / cols_per_tile;
+    p.nw = 4;
     p.ksplit = 1;
+    p.bm = expected_rows_per_group <= 32 ? 32 : expected_rows_per_group <= 64 ? 64 : 128;
+    auto cols = [&](int nw) { return (epi == Epi::SWIGLU ? 32 : 64) * nw; };
+    // Compute-bound shapes: 128-row tiles on 8 wavefronts (two per SIMD)
+    // when that still gives every CU a couple of workgroups.
+    if (e == Elem::BF16 && expected_rows_per_group >= 128) {
+        const int64_t blocks8 = (rows_upper / 128) * ((N + cols(8) - 1) / cols(8));
+        if (blocks8 >= 512) {
+            p.bm = 128;
+            p.nw = 8;
+        }
+    }
+    p.n_tiles = (N + cols(p.nw) - 1) / cols(p.nw);
     // sum_g ceil(rows_g / bm) <= rows_upper / bm + n_groups
     const int64_t m_tiles = rows_upper / p.bm + n_groups;
     p.grid = ((m_tiles * p.n_tiles + 7) / 8) * 8;
@@ -388,6 +538,7 @@ GemmPlan plan_gemm(Elem e, Epi epi, int64_t rows_upper, int n_groups, int64_t ex
 
 GemmPlan plan_dense_splitk(int64_t T, int N, int K, int chunk) {
     GemmPlan p;
+    p.nw = 4;
     p.bm = T <= 32 ? 32 : T <= 1024 ? 64 : 128;
     p.n_tiles = (N + 255) / 256;
     const int64_t tiles = (T + p.bm - 1) / p.bm * p.n_tiles;

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include <hip/hip_runtime.h>
@@ -202,13 +204,12 @@ hipError_t do_dispatch(const moe_config* c, int64_t T, const int32_t* ids, int32
     return launch_dispatch(d, s);
 }
 
-hipError_t do_expert_ffn(const moe_config* c, int64_t T, const void* x, const int32_t* perm,
-                         const int32_t* offsets, const moe_weights* wt, void* rows, void* shared_out, void* ws,
-                         hipStream_t s) {
+hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const int32_t* perm,
+                         const int32_t* offsets, const moe_weights* wt, void* rows, void* ws, hipStream_t s) {
     const Layout L = layout(c, T);
     const Elem el = gemm_elem(c);
     const int El = c->expert_end - c->expert_begin;
-    const int64_t H = c->hidden, I = c->inter, Is = c->shared_inter;
+    const int64_t H = c->hidden, I = c->inter;
     const int64_t P = T * c->top_k;
     int32_t* sched = at<int32_t>(ws, L.sched);
     hipError_t e;
@@ -251,45 +252,117 @@ hipError_t do_expert_ffn(const moe_config* c, int64_t T, const void* x, const in
     g2.ldc = static_cast<int>(H);
     g2.out_f32 = c->dtype == MOE_DTYPE_F32;
     GemmPlan p2 = plan_gemm(el, Epi::PLAIN, P, El, per_expert, static_cast<int>(H));
-    p2.bm = p1.bm;       // same m-tiles as the schedule
-    p2.grid = ((P / p2.bm + El) * p2.n_tiles + 7) / 8 * 8;
-    {
-        StageTimer tm(MOE_STAGE_DOWN, s);
-        if ((e = launch_gemm(el, Epi::PLAIN, g2, p2, s)) != hipSuccess) return e;
+    if (p2.bm != p1.bm) {    // the down GEMM reuses the gate/up schedule's m-tiles
+        p2.bm = p1.bm;
+        p2.nw = p1.nw;
+        p2.n_tiles = (static_cast<int>(H) + 64 * p2.nw - 1) / (64 * p2.nw);
+        p2.grid = ((P / p2.bm + El) * p2.n_tiles + 7) / 8 * 8;
     }
+    StageTimer tm(MOE_STAGE_DOWN, s);
+    return launch_gemm(el, Epi::PLAIN, g2, p2, s);
+}
 
-    // Shared expert: every token, a single group (no schedule needed).
-    if (Is > 0) {
-        GemmArgs s1{};
-        s1.A = s1.A_shared = x;
-        s1.B = s1.B_shared = wt->shared_w13;
-        s1.n_local = 0;
-        s1.has_shared = 1;
-        s1.T = static_cast<int>(T);
-        s1.K = static_cast<int>(H);
-        s1.N = static_cast<int>(Is);
-        s1.inter = static_cast<int>(Is);
-        s1.C = s1.C_shared = at<void>(ws, L.h_shared);
-        s1.ldc = static_cast<int>(Is);
-        const GemmPlan q1 = plan_gemm(el, Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
-        {
-            StageTimer tm(MOE_STAGE_SHARED_GATE_UP, s);
-            if ((e = launch_gemm(el, Epi::SWIGLU, s1, q1, s)) != hipSuccess) return e;
-        }
-        GemmArgs s2 = s1;
-        s2.A = s2.A_shared = at<void>(ws, L.h_shared);
-        s2.B = s2.B_shared = wt->shared_w2;
-        s2.K = static_cast<int>(Is);
-        s2.N = static_cast<int>(H);
-        s2.inter = 0;
-        s2.C = s2.C_shared = shared_out;
-        s2.ldc = static_cast<int>(H);
-        s2.out_f32 = 1;          // the shared output stays fp32 (it is never exchanged)
-        const GemmPlan q2 = plan_gemm(el, Epi::PLAIN, T, 1, T, static_cast<int>(H));
-        StageTimer tm(MOE_STAGE_SHARED_DOWN, s);
-        if ((e = launch_gemm(el, Epi::PLAIN, s2, q2, s)) != hipSuccess) return e;
+// Shared expert: every token, a single group (no schedule needed).
+hipError_t do_shared_ffn(const moe_config* c, int64_t T, const void* x, const moe_weights* wt, void* shared_out,
+                         void* ws, hipStream_t s) {
+    const Layout L = layout(c, T);
+    const Elem el = gemm_elem(c);
+    const int64_t H = c->hidden, Is = c->shared_inter;
+    hipError_t e;
+    GemmArgs s1{};
+    s1.A = s1.A_shared = x;
+    s1.B = s1.B_shared = wt->shared_w13;
+    s1.n_local = 0;
+    s1.has_shared = 1;
+    s1.T = static_cast<int>(T);
+    s1.K = static_cast<int>(H);
+    s1.N = static_cast<int>(Is);
+    s1.inter = static_cast<int>(Is);
+    s1.C = s1.C_shared = at<void>(ws, L.h_shared);
+    s1.ldc = static_cast<int>(Is);
+    const GemmPlan q1 = plan_gemm(el, Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
+    {
+        StageTimer tm(MOE_STAGE_SHARED_GATE_UP, s);
+        if ((e = launch_gemm(el, Epi::SWIGLU, s1, q1, s)) != hipSuccess) return e;
     }
+    GemmArgs s2 = s1;
+    s2.A = s2.A_shared = at<void>(ws, L.h_shared);
+    s2.B = s2.B_shared = wt->shared_w2;
+    s2.K = static_cast<int>(Is);
+    s2.N = static_cast<int>(H);
+    s2.inter = 0;
+    s2.C = s2.C_shared = shared_out;
+    s2.ldc = static_cast<int>(H);
+    s2.out_f32 = 1;          // the shared output stays fp32 (it is never exchanged)
+    const GemmPlan q2 = plan_gemm(el, Epi::PLAIN, T, 1, T, static_cast<int>(H));
+    StageTimer tm(MOE_STAGE_SHARED_DOWN, s);
+    return launch_gemm(el, Epi::PLAIN, s2, q2, s);
+}
+
+// The shared expert runs on a second stream of the same device, concurrently
+// with the routed path (NVIDIA "Optimizing DeepSeek R1 throughput on
+// Blackwell", section "Multi-stream": shared and routed experts on two
+// streams; Perplexity, "Overlapping compute and communication": the shared
+// expert fills the dispatch gap). The stream and its two events are created
+// on first use on a device and kept until the process ends.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::unordered_map<int, SideStream> g_side;
+
+hipError_t side_stream(SideStream** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    SideStream& ss = g_side[dev];
+    if (!ss.stream) {
+        if ((e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    *out = &ss;
     return hipSuccess;
+}
+
+// Launches the shared expert on the side stream, ordered after everything
+// already on `s`; the caller joins with join_shared before reading shared_out.
+hipError_t fork_shared(const moe_config* c, int64_t T, const void* x, const moe_weights* wt, void* shared_out,
+                       void* ws, hipStream_t s, SideStream** side) {
+    hipError_t e = side_stream(side);
+    if (e != hipSuccess) return e;
+    SideStream* ss = *side;
+    if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ss->stream, ss->fork, 0)) != hipSuccess) return e;
+    if ((e = do_shared_ffn(c, T, x, wt, shared_out, ws, ss->stream)) != hipSuccess) return e;
+    return hipEventRecord(ss->join, ss->stream);
+}
+
+hipError_t join_shared(SideStream* ss, hipStream_t s) { return hipStreamWaitEvent(s, ss->join, 0); }
+
+// Overlap pays when the routed experts stream weights from HBM (few rows per
+// expert) while the shared expert is compute-bound; at prefill shapes both
+// are compute-bound and run one after the other.
+bool overlap_shared(const moe_config* c, int64_t T) {
+    return c->shared_inter > 0 && T * c->top_k < 128LL * c->n_experts;
+}
+
+hipError_t do_expert_ffn(const moe_config* c, int64_t T, const void* x, const int32_t* perm,
+                         const int32_t* offsets, const moe_weights* wt, void* rows, void* shared_out, void* ws,
+                         hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    SideStream* side = nullptr;
+    hipError_t e = hipSuccess;
+    if (overlap_shared(c, T) && (e = fork_shared(c, T, x, wt, shared_out, ws, s, &side)) != hipSuccess) return e;
+    e = do_routed_ffn(c, T, x, perm, offsets, wt, rows, ws, s);
+    if (side) {
+        const hipError_t j = join_shared(side, s);
+        if (e == hipSuccess) e = j;
+    } else if (e == hipSuccess && c->shared_inter > 0) {
+        e = do_shared_ffn(c, T, x, wt, shared_out, ws, s);
+    }
+    return e;
 }
 
 hipError_t do_combine(const moe_config* c, int64_t T, const void* rows, const int32_t* inv, const float* w,
@@ -434,16 +507,27 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
     int32_t* inv = at<int32_t>(ws, L.inv);
     void* rows = at<void>(ws, L.rows);
     void* shared_out = cfg->shared_inter > 0 ? at<void>(ws, L.shared_out) : nullptr;
-    hipError_t e;
-    if ((e = do_router_gemm(cfg, T, x, w_router, router_bias, logits, ws, stream)) != hipSuccess) return MOE_ERR_HIP;
-    if ((e = do_route(cfg, T, logits, score_bias, ids, w, stream)) != hipSuccess) return MOE_ERR_HIP;
-    if ((e = do_dispatch(cfg, T, ids, at<int32_t>(ws, L.raw), at<int32_t>(ws, L.counts), offsets, perm, inv, ws,
-                         stream)) != hipSuccess)
-        return MOE_ERR_HIP;
-    if ((e = do_expert_ffn(cfg, T, x, perm, offsets, weights, rows, shared_out, ws, stream)) != hipSuccess)
-        return MOE_ERR_HIP;
-    if ((e = do_combine(cfg, T, rows, inv, w, shared_out, y, stream)) != hipSuccess) return MOE_ERR_HIP;
-    return MOE_OK;
+    // The small routing kernels run first, alone on the GPU; then the shared
+    // expert (which needs only x) runs on the side stream concurrently with
+    // the routed experts' grouped GEMMs.
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    SideStream* side = nullptr;
+    hipError_t e = do_router_gemm(cfg, T, x, w_router, router_bias, logits, ws, stream);
+    if (e == hipSuccess) e = do_route(cfg, T, logits, score_bias, ids, w, stream);
+    if (e == hipSuccess)
+        e = do_dispatch(cfg, T, ids, at<int32_t>(ws, L.raw), at<int32_t>(ws, L.counts), offsets, perm, inv, ws,
+                        stream);
+    const bool overlap = overlap_shared(cfg, T);
+    if (e == hipSuccess && overlap) e = fork_shared(cfg, T, x, weights, shared_out, ws, stream, &side);
+    if (e == hipSuccess) e = do_routed_ffn(cfg, T, x, perm, offsets, weights, rows, ws, stream);
+    if (side) {
+        const hipError_t j = join_shared(side, stream);     // always rejoin the side stream
+        if (e == hipSuccess) e = j;
+    } else if (e == hipSuccess && shared_out) {
+        e = do_shared_ffn(cfg, T, x, weights, shared_out, ws, stream);
+    }
+    if (e == hipSuccess) e = do_combine(cfg, T, rows, inv, w, shared_out, y, stream);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int moe_profile_enable(int max_records) {

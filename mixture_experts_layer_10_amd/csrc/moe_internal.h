@@ -86,6 +86,7 @@ struct GemmArgs {
 
 struct GemmPlan {
     int bm;                   // rows per tile
+    int nw;                   // wavefronts per workgroup (4 or 8)
     int n_tiles;              // column tiles per group
     int ksplit;               // K slices per tile
     int64_t grid;             // workgroups launched (upper bound on tiles * ksplit)

@@ -5,7 +5,9 @@ Recipe (the pages name no dataset for this layer; these stand in for it):
   * router weight W_r [E, H] and expert weights ~ N(0, 1/fan_in), fan_in = H
     for W_r and the gate/up stack W13 [E_l, 2I, H], I for the down projection
     W2 [E_l, H, I]; the shared expert uses the same rule;
-  * selection-only score bias b_e: absent, zero, or N(0, 0.1^2);
+  * selection-only score bias b_e: absent, zero, or N(0, s^2) with s = 0.01
+    (decode workloads: it changes the selection of about half the tokens while
+    the load stays near-uniform, as a balancing bias intends) or s = 0.1;
   * router linear bias c_e: absent, or a Zipf(s = 1.1) popularity offset
     -1.1 * ln(rank_e) with rank_e = 1 + a seeded permutation of the experts;
   * bf16 tensors are the float32 draws rounded to nearest-even by torch;
@@ -93,8 +95,8 @@ def make_inputs(w, device="cpu", seed=0):
         out["score_bias"] = None
     elif sb == "zero":
         out["score_bias"] = torch.zeros(E, dtype=torch.float32, device=device)
-    elif sb == "normal0.1":
-        out["score_bias"] = _normal((E,), 0.1, device, seed, "score_bias")
+    elif sb in ("normal0.01", "normal0.1"):
+        out["score_bias"] = _normal((E,), float(sb[6:]), device, seed, "score_bias")
     else:
         raise ValueError(sb)
 

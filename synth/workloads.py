@@ -22,7 +22,7 @@ Keys:
   shared_inter I_s, shared-expert intermediate size (0 = no shared expert)
   dtype        "f32", "bf16" or "fp8" (weights; activations follow)
   capacity_factor  <= 0 means no capacity limit
-  score_bias   "none", "zero" or "normal0.1" (selection-only bias)
+  score_bias   "none", "zero", "normal0.01" or "normal0.1" (selection-only bias)
   router_bias  "none" or "zipf1.1" (linear bias of the router GEMM)
 """
 
@@ -42,10 +42,10 @@ WORKLOADS = {
         capacity_factor=0.0, score_bias="none", router_bias="none"),
     # One GPU's EP8 share (routed experts 0..31) of a DeepSeek-V3 layer, decode.
     "ep8_decode_bf16": dict(_BASE_DSV3, T=2048, expert_begin=0, expert_end=32,
-                            dtype="bf16", score_bias="normal0.1"),
+                            dtype="bf16", score_bias="normal0.01"),
     # Whole 256-expert layer on one GPU, decode batch (~16 rows per expert).
     "full_decode_bf16": dict(_BASE_DSV3, T=512, expert_begin=0, expert_end=256,
-                             dtype="bf16", score_bias="normal0.1"),
+                             dtype="bf16", score_bias="normal0.01"),
     # Same layer at prefill shape (~512 rows per expert).
     "full_prefill_bf16": dict(_BASE_DSV3, T=16384, expert_begin=0, expert_end=256,
                               dtype="bf16", score_bias="zero"),

@@ -251,3 +251,40 @@ def test_expert_parallel_shares_sum_to_whole_layer():
     d = (acc - (EP - 1) * rs - y_full.double()).abs().max().item()
     rms = y_full.double().pow(2).mean().sqrt().item()
     assert d / rms < 1e-5
+
+
+def test_forward_graph_capture_replays_match_eager():
+    """moe_forward enqueues without host synchronisation: it can be captured
+    in a HIP graph (side stream included) and every replay, with eager work
+    between replays, equals the eager result bit for bit."""
+    w = _small(T=200)
+    run = Run(w)
+    y_eager = run.forward()
+    torch.cuda.synchronize()
+    y_eager = y_eager.clone()
+    y = torch.empty_like(y_eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run.forward(y=y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.forward(y=y)
+    for _ in range(3):
+        y.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager)
+        run.forward()                    # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_forward_is_deterministic():
+    w = workload("ep8_decode_bf16", T=256)
+    run = Run(w, gen_device="cuda")
+    ys = [run.forward().clone() for _ in range(5)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
