@@ -197,6 +197,17 @@ int moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const int32_
 int moe_combine(const moe_config* cfg, int64_t T, const void* out_rows, const int32_t* inv,
                 const float* topk_w, const void* shared_out, void* y, hipStream_t stream);
 
+/* FP8 activation quantisation (Perplexity, section "Quantization": dynamic
+ * scales per 1x128 vector, computed online): for each row and each block of
+ * 128 columns, a = max |x|; scale = a / 448 and codes = e4m3(x * (448 / a))
+ * (OCP E4M3FN, round to nearest even; every step one float32 operation),
+ * or scale 1 and zero codes when a == 0.
+ *  x [rows, H] bf16 device; q [rows, H] uint8 codes out; scale [rows, H/128]
+ *  fp32 out. moe_expert_ffn and moe_forward apply the same quantisation to x
+ *  internally when cfg->dtype is MOE_DTYPE_FP8. */
+int moe_quantize_fp8(const moe_config* cfg, int64_t rows, const void* x, uint8_t* q, float* scale,
+                     hipStream_t stream);
+
 /* The whole layer: router GEMM, route, dispatch, experts, combine.
  *  x [T, H], w_router [E, H] (activation type; bf16 for FP8), router_bias [E]
  *  and score_bias [E] fp32 or NULL, weights as above; y [T, H] out.
@@ -224,7 +235,8 @@ enum moe_stage {
     MOE_STAGE_SHARED_GATE_UP = 5,
     MOE_STAGE_SHARED_DOWN = 6,
     MOE_STAGE_COMBINE = 7,
-    MOE_STAGE_COUNT = 8
+    MOE_STAGE_QUANT = 8,            /* FP8: activation quantisation of x */
+    MOE_STAGE_COUNT = 9
 };
 int moe_profile_enable(int max_records);
 int moe_profile_reset(void);

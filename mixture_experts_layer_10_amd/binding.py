@@ -70,6 +70,7 @@ def lib():
             "moe_expert_ffn": (ctypes.c_int, [cfgp, i64, vp, i32p, i32p, wp, vp, vp, vp, ctypes.c_size_t, vp]),
             "moe_combine": (ctypes.c_int, [cfgp, i64, vp, i32p, fp, vp, vp, vp]),
             "moe_forward": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, wp, vp, fp, i32p, vp, ctypes.c_size_t, vp]),
+            "moe_quantize_fp8": (ctypes.c_int, [cfgp, i64, vp, vp, fp, vp]),
             "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
             "moe_profile_reset": (ctypes.c_int, []),
             "moe_profile_query": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
@@ -265,6 +266,15 @@ def moe_combine(cfg, out_rows, inv, topk_w, shared_out, y, stream=None):
         _ptr(y, _out_dtype(cfg), (T, H), "y"), _stream(stream)), "moe_combine")
 
 
+def moe_quantize_fp8(cfg, x, q, scale, stream=None):
+    """x [rows, H] bf16 -> e4m3 codes q [rows, H] (uint8) and scales [rows, H/128] (fp32)."""
+    rows, H = x.shape
+    _check(lib().moe_quantize_fp8(
+        ctypes.byref(cfg), rows, _ptr(x, torch.bfloat16, (rows, cfg.hidden), "x"),
+        _ptr(q, torch.uint8, (rows, H), "q"), _ptr(scale, torch.float32, (rows, H // 128), "scale"),
+        _stream(stream)), "moe_quantize_fp8")
+
+
 def moe_forward(cfg, x, w_router, router_bias, score_bias, weights, y, ws, logits_out=None,
                 topk_ids_out=None, stream=None):
     T = x.shape[0]
@@ -284,7 +294,8 @@ def moe_forward(cfg, x, w_router, router_bias, score_bias, weights, y, ws, logit
 # Diagnostics: per-stage HIP-event timing
 # ---------------------------------------------------------------------------
 
-STAGES = ["router_gemm", "route", "dispatch", "gate_up", "down", "shared_gate_up", "shared_down", "combine"]
+STAGES = ["router_gemm", "route", "dispatch", "gate_up", "down", "shared_gate_up", "shared_down", "combine",
+          "quant"]
 
 
 def profile_enable(max_records):

@@ -43,7 +43,7 @@
 #include <type_traits>
 #include <utility>
 
-#include "moe_device.h"
+#include "gemm_tile.h"
 
 namespace moe {
 namespace {
@@ -119,43 +119,12 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
     const int lr = lane & 15, lq = lane >> 4;
 
     // ---- tile lookup -----------------------------------------------------
-    // Work items are (group, n-tile, m-tile, k-slice), k-slice fastest, then
-    // m-tile: the blocks that stream the same weight panel run side by side.
-    // Items are dealt to the 8 XCDs in contiguous ranges (the hardware deals
-    // blocks round-robin), so neighbouring items share an XCD's L2.
+    Tile tl;
+    if (!find_tile(a, n_tiles, BM, tl)) return;
+    const int g = tl.g, ks = tl.ks, nt = tl.nt;
+    const bool shared = tl.shared;
+    const int row0 = tl.row0, m0 = tl.m0, rows = tl.rows;
     const int KS = a.ksplit;
-    const int n_groups = a.n_local + a.has_shared;
-    const int per_item = n_tiles * KS;                 // items per m-tile
-    // A null schedule means a single group of T rows.
-    const int total = (a.sched ? a.sched[n_groups] : (a.T + BM - 1) / BM) * per_item;
-    const int per_xcd = (total + 7) >> 3;
-    const int slot = static_cast<int>(blockIdx.x >> 3);
-    if (slot >= per_xcd) return;
-    const int L = static_cast<int>(blockIdx.x & 7) * per_xcd + slot;
-    if (L >= total) return;
-    int g = 0, mt_begin = 0, mt_count = (a.T + BM - 1) / BM;
-    if (a.sched) {
-        int lo = 0, hi = n_groups;                     // sched[lo]*per_item <= L < sched[hi]*per_item
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (a.sched[mid] * per_item <= L) lo = mid; else hi = mid;
-        }
-        g = lo;
-        mt_begin = a.sched[g];
-        mt_count = a.sched[g + 1] - mt_begin;
-    }
-    const int local = L - mt_begin * per_item;
-    const int ks = local % KS;
-    const int nt = (local / KS) / mt_count;
-    const int mt = (local / KS) - nt * mt_count;
-    const bool shared = a.has_shared && g == a.n_local;
-    int row0 = 0, rows_g = a.T;
-    if (!shared && a.offsets) {
-        row0 = a.offsets[g];
-        rows_g = a.offsets[g + 1] - row0;
-    }
-    const int m0 = mt * BM;
-    const int rows = min(BM, rows_g - m0);
     const int nrf = (rows + 15) >> 4;
     const int K = a.K;
     const int nch_all = K / T::kChunk;

@@ -1,0 +1,357 @@
+// FP8 path: activation quantiser (K4) and the block-scaled grouped GEMM
+// (K5/K6 with e4m3 operands) on gfx950 MFMA.
+//
+// What it computes: Perplexity "Lower latency and higher throughput with
+// multi-node DeepSeek deployment", section "Quantization": weights carry one
+// static scale per 128x128 block, activations one dynamic scale per 1x128
+// vector computed online; for an (M, K) x (K, N) product the activation scales
+// are (M, K/128) and the weight scales (K/128, N/128), and the SiLU kernel
+// quantises its output per 128-element block. Formats: OCP E4M3FN (bias 7,
+// largest finite value 448), round to nearest even; a block's scale is
+// amax / 448 and its codes are e4m3(v * (448 / amax)), an all-zero block gets
+// scale 1 and zero codes.
+//
+// GEMM structure: as the bf16 kernel (weights streamed into VGPRs, gathered
+// activation tile in LDS, tiles dealt per XCD), with a K chunk of 128 = one
+// scale block: each 16x16 output fragment takes one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per chunk (unit E8M0 scales) into a zeroed
+// temporary, which is added to the fp32 accumulator times
+// a_scale[row] * w_scale[column block] (the block dequantisation in fp32).
+#include <float.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "gemm_tile.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 128;            // K per chunk = one scale block
+constexpr int kRowB = 128;             // LDS bytes per A row per chunk
+typedef int i32x8v __attribute__((ext_vector_type(8)));
+
+// Two 16-byte loads straight into the 8 registers of one MFMA operand.
+__device__ __forceinline__ i32x8v ld32(const void* lo, const void* hi) {
+    typedef int i32x4v __attribute__((ext_vector_type(4)));
+    const i32x4v a = *reinterpret_cast<const i32x4v*>(lo);
+    const i32x4v b = *reinterpret_cast<const i32x4v*>(hi);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Two floats -> two e4m3 codes (round to nearest even, saturating at +-448),
+// packed in the low 16 bits.
+__device__ __forceinline__ uint32_t cvt2_e4m3(float a, float b) {
+    a = fminf(fmaxf(a, -448.0f), 448.0f);
+    b = fminf(fmaxf(b, -448.0f), 448.0f);
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xffffu;
+}
+
+// 448 / amax for a block with amax > 0; a block below about 2**-119, where
+// the quotient overflows float32, takes the largest finite float32.
+__device__ __forceinline__ float fp8_inv_scale(float amax) { return fminf(448.0f / amax, FLT_MAX); }
+
+// ---- K4: per (row, 128-column block) quantisation of bf16 activations ------
+// One workgroup per row; 16 lanes per 128-column block, 8 values per lane.
+__global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* x, uint8_t* q, float* scale,
+                                                             int cols) {
+    const int64_t row = blockIdx.x;
+    const int nblk = cols / 128;
+    const int sub = threadIdx.x & 15;
+    for (int blk = threadIdx.x >> 4; blk < nblk; blk += kThreads / 16) {
+        const int64_t off = row * cols + blk * 128 + sub * 8;
+        const vec16 v = ld16(x + off);
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = bf16_bits_to_f32(static_cast<uint16_t>(v.w[i] & 0xffffu));
+            f[2 * i + 1] = bf16_bits_to_f32(static_cast<uint16_t>(v.w[i] >> 16));
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+        const bool nz = amax > 0.0f;
+        const float inv = nz ? fp8_inv_scale(amax) : 0.0f;
+        uint32_t lo = 0, hi = 0;
+        if (nz) {
+            lo = cvt2_e4m3(f[0] * inv, f[1] * inv) | (cvt2_e4m3(f[2] * inv, f[3] * inv) << 16);
+            hi = cvt2_e4m3(f[4] * inv, f[5] * inv) | (cvt2_e4m3(f[6] * inv, f[7] * inv) << 16);
+        }
+        *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
+        if (sub == 0) scale[row * nblk + blk] = nz ? amax / 448.0f : 1.0f;
+    }
+}
+
+// ---- K5/K6 in e4m3 -----------------------------------------------------------
+template <Epi EPI, int BM, int PD>
+__global__ __launch_bounds__(kThreads, (BM <= 32 ? 2 : 1)) void gemm_fp8_kernel(GemmArgs a, int n_tiles) {
+    constexpr int ROWG = kRowB / 16;                   // 8 granules per A row
+    constexpr int NRF = BM / 16;
+    constexpr int ROWS_PER_PASS = kThreads / ROWG;     // 32
+    constexpr int PASSES = BM / ROWS_PER_PASS;
+    constexpr int NB = PD + 1;
+    constexpr int U = (NB % 2 == 0) ? NB : 2 * NB;
+    constexpr int APD = 2;
+    static_assert(BM % ROWS_PER_PASS == 0, "tile rows");
+
+    __shared__ __attribute__((aligned(16))) unsigned char s_a[2][BM * kRowB];
+    __shared__ __attribute__((aligned(16))) float s_sa[2][BM];      // activation scales of the chunk
+    __shared__ float s_amax[4][BM];                                 // SwiGLU epilogue: per-wave row amax
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    Tile tl;
+    if (!find_tile(a, n_tiles, BM, tl)) return;
+    const int g = tl.g, nt = tl.nt;
+    const bool shared = tl.shared;
+    const int row0 = tl.row0, m0 = tl.m0, rows = tl.rows;
+    const int nrf = (rows + 15) >> 4;
+    const int K = a.K;
+    const int nch = K / kChunk;
+    const int kblocks = K / 128;
+
+    // ---- weights: e4m3 rows + fp32 scales per 128x128 block ---------------
+    const int nb_rows = (EPI == Epi::SWIGLU ? 2 * a.inter : a.N) / 128;      // scale rows per expert
+    const unsigned char* Bg = shared ? static_cast<const unsigned char*>(a.B_shared)
+                                     : static_cast<const unsigned char*>(a.B) + static_cast<int64_t>(g) * a.b_stride;
+    const float* Sg = shared ? a.B_scale_shared : a.B_scale + static_cast<int64_t>(g) * nb_rows * kblocks;
+    uint32_t boff[4];
+    const float* bsc[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        int brow;
+        if constexpr (EPI == Epi::SWIGLU) {
+            const int n0 = nt * 128 + wave * 32;
+            brow = (f < 2) ? n0 + 16 * f + lr : a.inter + n0 + 16 * (f - 2) + lr;
+        } else {
+            brow = nt * 256 + wave * 64 + 16 * f + lr;
+            brow = brow < a.N ? brow : a.N - 1;
+        }
+        boff[f] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K) + lq * 16;
+        bsc[f] = Sg + (brow / 128) * kblocks;          // 16 rows of a fragment share a 128-row block
+    }
+
+    // ---- activations: gathered e4m3 rows and their per-block scales --------
+    const int aj = tid % ROWG, ar = tid / ROWG;
+    const unsigned char* Abase = static_cast<const unsigned char*>(shared ? a.A_shared : a.A) + aj * 16;
+    const float* Ascale = shared ? a.A_scale_shared : a.A_scale;
+    auto src_row = [&](int r) -> uint32_t {
+        r = r < rows ? r : rows - 1;
+        if (shared) return m0 + r;
+        if (a.gather) return static_cast<uint32_t>(a.perm[row0 + m0 + r] / a.topk);
+        return row0 + m0 + r;
+    };
+    uint32_t aoff[PASSES];
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) aoff[i] = src_row(ar + i * ROWS_PER_PASS) * static_cast<uint32_t>(K);
+    const float* sa_src = tid < BM ? Ascale + static_cast<int64_t>(src_row(tid)) * kblocks : Ascale;
+    // LDS: row r's granule j sits at j ^ (r & 7).
+    const int a_st = ar * kRowB + ((aj ^ (ar & 7)) * 16);
+    int a_ld[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) a_ld[s] = lr * kRowB + (((s * 4 + lq) ^ (lr & 7)) * 16);
+
+    f32x4 acc[NRF][4];
+#pragma unroll
+    for (int i = 0; i < NRF; ++i)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    i32x8v breg[NB][4];
+    float bsreg[NB][4];
+    vec16 areg[APD][PASSES];
+    float sareg[APD];
+    const int last = nch - 1;
+
+    auto load_b = [&](i32x8v (&dst)[4], float (&ds)[4], int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const unsigned char* p = Bg + boff[f] + static_cast<int64_t>(c) * kChunk;
+            dst[f] = ld32(p, p + 64);
+            ds[f] = bsc[f][c];
+        }
+    };
+    auto load_a = [&](vec16 (&dst)[PASSES], float& ds, int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < PASSES; ++i) dst[i] = ld16(Abase + aoff[i] + static_cast<int64_t>(c) * kChunk);
+        ds = sa_src[c];
+    };
+    auto store_a = [&](const vec16 (&src)[PASSES], float ds, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < PASSES; ++i) st16(&s_a[buf][a_st + i * ROWS_PER_PASS * kRowB], src[i]);
+        if (tid < BM) s_sa[buf][tid] = ds;
+    };
+    auto compute = [&](const i32x8v (&bv)[4], const float (&bs)[4], int buf) __attribute__((always_inline)) {
+        const unsigned char* src = s_a[buf];
+        i32x8v af[2];
+        f32x4 sa[2];
+        af[0] = ld32(src + a_ld[0], src + a_ld[1]);
+        sa[0] = *reinterpret_cast<const f32x4*>(&s_sa[buf][4 * lq]);
+#pragma unroll
+        for (int i = 0; i < NRF; ++i) {
+            if (i == 0 || i < nrf) {
+                if (i + 1 < NRF) {
+                    af[(i + 1) & 1] = ld32(src + (i + 1) * 16 * kRowB + a_ld[0], src + (i + 1) * 16 * kRowB + a_ld[1]);
+                    sa[(i + 1) & 1] = *reinterpret_cast<const f32x4*>(&s_sa[buf][(i + 1) * 16 + 4 * lq]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const i32x8v av = af[i & 1];
+                f32x4 t[4];
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                    t[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[f], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                           0, 127, 0, 127);
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[i][f][v] += t[f][v] * (sa[i & 1][v] * bs[f]);
+            }
+        }
+    };
+
+    // ---- main loop (branch-free steady state; see the bf16 kernel) --------
+    auto step = [&](auto uc, int c) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        load_a(areg[u % APD], sareg[u % APD], min(c + APD, last));
+        load_b(breg[(u + PD) % NB], bsreg[(u + PD) % NB], min(c + PD, last));
+        compute(breg[u % NB], bsreg[u % NB], u & 1);
+        store_a(areg[(u + 1) % APD], sareg[(u + 1) % APD], (u + 1) & 1);
+        __syncthreads();
+    };
+    if (nch > 0) {
+#pragma unroll
+        for (int p = 0; p < APD; ++p) load_a(areg[p], sareg[p], min(p, last));
+#pragma unroll
+        for (int p = 0; p < PD; ++p) load_b(breg[p], bsreg[p], min(p, last));
+        store_a(areg[0], sareg[0], 0);
+        __syncthreads();
+    }
+    int c = 0;
+    for (; c + U <= nch; c += U) {
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            (step(std::integral_constant<int, I>{}, c + I), ...);
+        }(std::make_integer_sequence<int, U>{});
+    }
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((c + I < nch ? step(std::integral_constant<int, I>{}, c + I) : void()), ...);
+    }(std::make_integer_sequence<int, U>{});
+
+    // ---- epilogue ------------------------------------------------------------
+    const int64_t crow0 = shared ? m0 : static_cast<int64_t>(row0) + m0;
+    if constexpr (EPI == Epi::SWIGLU) {
+        // h = silu(g) * u in fp32, then e4m3 with one scale per (row, 128
+        // columns): this tile's 128 h columns are exactly one scale block.
+        float h[NRF][2][4];
+#pragma unroll
+        for (int i = 0; i < NRF; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float m = 0.0f;
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    const float gv = acc[i][f][v], uv = acc[i][f + 2][v];
+                    h[i][f][v] = gv / (1.0f + __expf(-gv)) * uv;
+                    m = fmaxf(m, fabsf(h[i][f][v]));
+                }
+#pragma unroll
+                for (int s = 1; s < 16; s <<= 1) m = fmaxf(m, __shfl_xor(m, s, 16));
+                if (lr == 0) s_amax[wave][i * 16 + lq * 4 + v] = m;
+            }
+        __syncthreads();
+        uint8_t* Cq = static_cast<uint8_t*>(shared ? a.C_shared : a.C);
+        float* Cs = shared ? a.C_scale_shared : a.C_scale;
+        const int nsb = a.N / 128;
+#pragma unroll
+        for (int i = 0; i < NRF; ++i) {
+            if (i < nrf) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = i * 16 + lq * 4 + v;
+                    const float amax =
+                        fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
+                    const bool nz = amax > 0.0f;
+                    const float inv = nz ? fp8_inv_scale(amax) : 0.0f;
+                    if (r < rows) {
+#pragma unroll
+                        for (int f = 0; f < 2; ++f) {
+                            const int col = nt * 128 + wave * 32 + 16 * f + lr;
+                            const uint32_t code = nz ? (cvt2_e4m3(h[i][f][v] * inv, 0.0f) & 0xffu) : 0u;
+                            Cq[(crow0 + r) * a.ldc + col] = static_cast<uint8_t>(code);
+                        }
+                        if (wave == 0 && lr == 0) Cs[(crow0 + r) * nsb + nt] = nz ? amax / 448.0f : 1.0f;
+                    }
+                }
+            }
+        }
+    } else {
+        unsigned char* Cb = static_cast<unsigned char*>(shared ? a.C_shared : a.C);
+#pragma unroll
+        for (int i = 0; i < NRF; ++i) {
+            if (i < nrf) {
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const int col = nt * 256 + wave * 64 + 16 * f + lr;
+                    if (col < a.N) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int r = i * 16 + lq * 4 + v;
+                            if (r < rows) {
+                                const int64_t off = (crow0 + r) * a.ldc + col;
+                                if (a.out_f32)
+                                    reinterpret_cast<float*>(Cb)[off] = acc[i][f][v];
+                                else
+                                    reinterpret_cast<uint16_t*>(Cb)[off] = f32_to_bf16_bits(acc[i][f][v]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <Epi EPI>
+hipError_t launch_fp8_bm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(p.grid)), block(kThreads);
+    switch (p.bm) {
+        case 32: hipLaunchKernelGGL((gemm_fp8_kernel<EPI, 32, 1>), grid, block, 0, s, a, p.n_tiles); break;
+        case 64: hipLaunchKernelGGL((gemm_fp8_kernel<EPI, 64, 1>), grid, block, 0, s, a, p.n_tiles); break;
+        case 128: hipLaunchKernelGGL((gemm_fp8_kernel<EPI, 128, 1>), grid, block, 0, s, a, p.n_tiles); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* q, float* scale, int64_t rows, int cols, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_fp8_kernel, dim3(static_cast<unsigned>(rows)), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(x_bf16), q, scale, cols);
+    return hipGetLastError();
+}
+
+GemmPlan plan_gemm_fp8(Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N) {
+    GemmPlan p;
+    p.nw = 4;
+    p.ksplit = 1;
+    p.bm = expected_rows_per_group <= 32 ? 32 : expected_rows_per_group <= 64 ? 64 : 128;
+    const int cols = epi == Epi::SWIGLU ? 128 : 256;
+    p.n_tiles = (N + cols - 1) / cols;
+    const int64_t m_tiles = rows_upper / p.bm + n_groups;
+    p.grid = ((m_tiles * p.n_tiles + 7) / 8) * 8;
+    return p;
+}
+
+hipError_t launch_gemm_fp8(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    if (p.grid == 0) return hipSuccess;
+    GemmArgs b = a;
+    b.ksplit = 1;
+    return epi == Epi::SWIGLU ? launch_fp8_bm<Epi::SWIGLU>(b, p, s) : launch_fp8_bm<Epi::PLAIN>(b, p, s);
+}
+
+}  // namespace moe

@@ -43,7 +43,6 @@ int validate(const moe_config* c) {
     if (c->top_k > 16 || c->n_experts > 512 || c->n_group > 64) return MOE_ERR_UNSUPPORTED;
     if (c->expert_end - c->expert_begin > 1024) return MOE_ERR_UNSUPPORTED;
     if (c->hidden % 128 != 0 || c->inter % 128 != 0 || c->shared_inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
-    if (c->dtype == MOE_DTYPE_FP8) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -54,7 +53,9 @@ Elem gemm_elem(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? Elem::F
 // Workspace layout for up to T tokens; every region 256-byte aligned.
 struct Layout {
     size_t logits, ids, w, raw, counts, offsets, perm, inv, chunk_hist, chunk_base, sched, partial;
-    size_t h, h_shared, rows, shared_out, total;
+    size_t h, h_shared, rows, shared_out;
+    size_t xq, xs, hs, hs_shared;       // FP8: quantised x and the scales of x and h
+    size_t total;
 };
 
 int router_chunk(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 64 : 128; }
@@ -87,6 +88,11 @@ Layout layout(const moe_config* c, int64_t T) {
     L.h_shared = take(static_cast<size_t>(act_bytes(c)) * T * c->shared_inter);
     L.rows = take(static_cast<size_t>(row_bytes(c)) * P * c->hidden);
     L.shared_out = take(sizeof(float) * T * c->hidden);
+    const bool fp8 = c->dtype == MOE_DTYPE_FP8;
+    L.xq = take(fp8 ? static_cast<size_t>(T) * c->hidden : 0);
+    L.xs = take(fp8 ? sizeof(float) * T * (c->hidden / 128) : 0);
+    L.hs = take(fp8 ? sizeof(float) * P * (c->inter / 128) : 0);
+    L.hs_shared = take(fp8 ? sizeof(float) * T * (c->shared_inter / 128) : 0);
     L.total = off;
     return L;
 }
@@ -232,6 +238,38 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
     g1.C = g1.C_shared = at<void>(ws, L.h);
     g1.ldc = static_cast<int>(I);
     const int64_t per_expert = (P + c->n_experts - 1) / c->n_experts;
+    if (c->dtype == MOE_DTYPE_FP8) {
+        // e4m3 operands: x quantised by the caller (moe_quantize_fp8 layout in
+        // the workspace), h requantised by the gate/up epilogue.
+        g1.A = g1.A_shared = at<void>(ws, L.xq);
+        g1.A_scale = g1.A_scale_shared = at<float>(ws, L.xs);
+        g1.B_scale = g1.B_scale_shared = wt->w13_scale;
+        g1.C_scale = g1.C_scale_shared = at<float>(ws, L.hs);
+        const GemmPlan p1 = plan_gemm_fp8(Epi::SWIGLU, P, El, per_expert, static_cast<int>(I));
+        if ((e = launch_schedule(g1, p1.bm, sched, s)) != hipSuccess) return e;
+        {
+            StageTimer tm(MOE_STAGE_GATE_UP, s);
+            if ((e = launch_gemm_fp8(Epi::SWIGLU, g1, p1, s)) != hipSuccess) return e;
+        }
+        GemmArgs g2 = g1;
+        g2.A = g2.A_shared = at<void>(ws, L.h);
+        g2.A_scale = g2.A_scale_shared = at<float>(ws, L.hs);
+        g2.perm = nullptr;
+        g2.gather = 0;
+        g2.B = g2.B_shared = wt->w2;
+        g2.B_scale = g2.B_scale_shared = wt->w2_scale;
+        g2.b_stride = H * I;
+        g2.K = static_cast<int>(I);
+        g2.N = static_cast<int>(H);
+        g2.inter = 0;
+        g2.C = g2.C_shared = rows;
+        g2.C_scale = g2.C_scale_shared = nullptr;
+        g2.ldc = static_cast<int>(H);
+        g2.out_f32 = 0;
+        GemmPlan p2 = plan_gemm_fp8(Epi::PLAIN, P, El, per_expert, static_cast<int>(H));
+        StageTimer tm(MOE_STAGE_DOWN, s);
+        return launch_gemm_fp8(Epi::PLAIN, g2, p2, s);
+    }
     const GemmPlan p1 = plan_gemm(el, Epi::SWIGLU, P, El, per_expert, static_cast<int>(I));
     if ((e = launch_schedule(g1, p1.bm, sched, s)) != hipSuccess) return e;
     {
@@ -280,6 +318,32 @@ hipError_t do_shared_ffn(const moe_config* c, int64_t T, const void* x, const mo
     s1.inter = static_cast<int>(Is);
     s1.C = s1.C_shared = at<void>(ws, L.h_shared);
     s1.ldc = static_cast<int>(Is);
+    if (c->dtype == MOE_DTYPE_FP8) {
+        s1.A = s1.A_shared = at<void>(ws, L.xq);
+        s1.A_scale = s1.A_scale_shared = at<float>(ws, L.xs);
+        s1.B_scale = s1.B_scale_shared = wt->shared_w13_scale;
+        s1.C_scale = s1.C_scale_shared = at<float>(ws, L.hs_shared);
+        const GemmPlan q1 = plan_gemm_fp8(Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
+        {
+            StageTimer tm(MOE_STAGE_SHARED_GATE_UP, s);
+            if ((e = launch_gemm_fp8(Epi::SWIGLU, s1, q1, s)) != hipSuccess) return e;
+        }
+        GemmArgs s2 = s1;
+        s2.A = s2.A_shared = at<void>(ws, L.h_shared);
+        s2.A_scale = s2.A_scale_shared = at<float>(ws, L.hs_shared);
+        s2.B = s2.B_shared = wt->shared_w2;
+        s2.B_scale = s2.B_scale_shared = wt->shared_w2_scale;
+        s2.K = static_cast<int>(Is);
+        s2.N = static_cast<int>(H);
+        s2.inter = 0;
+        s2.C = s2.C_shared = shared_out;
+        s2.C_scale = s2.C_scale_shared = nullptr;
+        s2.ldc = static_cast<int>(H);
+        s2.out_f32 = 1;
+        const GemmPlan q2 = plan_gemm_fp8(Epi::PLAIN, T, 1, T, static_cast<int>(H));
+        StageTimer tm(MOE_STAGE_SHARED_DOWN, s);
+        return launch_gemm_fp8(Epi::PLAIN, s2, q2, s);
+    }
     const GemmPlan q1 = plan_gemm(el, Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
     {
         StageTimer tm(MOE_STAGE_SHARED_GATE_UP, s);
@@ -348,12 +412,22 @@ bool overlap_shared(const moe_config* c, int64_t T) {
     return c->shared_inter > 0 && T * c->top_k < 128LL * c->n_experts;
 }
 
+// FP8: x -> e4m3 codes + per-(row, 128 columns) scales in the workspace,
+// read by both the routed and the shared gate/up GEMMs.
+hipError_t do_quant_x(const moe_config* c, int64_t T, const void* x, void* ws, hipStream_t s) {
+    if (c->dtype != MOE_DTYPE_FP8) return hipSuccess;
+    const Layout L = layout(c, T);
+    StageTimer tm(MOE_STAGE_QUANT, s);
+    return launch_quant_fp8(x, at<uint8_t>(ws, L.xq), at<float>(ws, L.xs), T, c->hidden, s);
+}
+
 hipError_t do_expert_ffn(const moe_config* c, int64_t T, const void* x, const int32_t* perm,
                          const int32_t* offsets, const moe_weights* wt, void* rows, void* shared_out, void* ws,
                          hipStream_t s) {
     std::lock_guard<std::mutex> lk(g_side_mu);
     SideStream* side = nullptr;
-    hipError_t e = hipSuccess;
+    hipError_t e = do_quant_x(c, T, x, ws, s);
+    if (e != hipSuccess) return e;
     if (overlap_shared(c, T) && (e = fork_shared(c, T, x, wt, shared_out, ws, s, &side)) != hipSuccess) return e;
     e = do_routed_ffn(c, T, x, perm, offsets, wt, rows, ws, s);
     if (side) {
@@ -388,6 +462,10 @@ bool weights_ok(const moe_config* c, const moe_weights* w) {
     if (c->shared_inter > 0 && (!w->shared_w13 || !w->shared_w2 || !aligned16(w->shared_w13) ||
                                 !aligned16(w->shared_w2)))
         return false;
+    if (c->dtype == MOE_DTYPE_FP8) {
+        if (!w->w13_scale || !w->w2_scale) return false;
+        if (c->shared_inter > 0 && (!w->shared_w13_scale || !w->shared_w2_scale)) return false;
+    }
     return true;
 }
 
@@ -518,6 +596,7 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
         e = do_dispatch(cfg, T, ids, at<int32_t>(ws, L.raw), at<int32_t>(ws, L.counts), offsets, perm, inv, ws,
                         stream);
     const bool overlap = overlap_shared(cfg, T);
+    if (e == hipSuccess) e = do_quant_x(cfg, T, x, ws, stream);
     if (e == hipSuccess && overlap) e = fork_shared(cfg, T, x, weights, shared_out, ws, stream, &side);
     if (e == hipSuccess) e = do_routed_ffn(cfg, T, x, perm, offsets, weights, rows, ws, stream);
     if (side) {
@@ -528,6 +607,17 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
     }
     if (e == hipSuccess) e = do_combine(cfg, T, rows, inv, w, shared_out, y, stream);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_quantize_fp8(const moe_config* cfg, int64_t rows, const void* x, uint8_t* q, float* scale,
+                     hipStream_t stream) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (rows < 0 || rows > INT32_MAX) return MOE_ERR_INVALID_ARG;
+    if (rows == 0) return MOE_OK;
+    if (!x || !q || !scale) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(scale)) return MOE_ERR_MISALIGNED;
+    return hip_status(launch_quant_fp8(x, q, scale, rows, cfg->hidden, stream));
 }
 
 int moe_profile_enable(int max_records) {

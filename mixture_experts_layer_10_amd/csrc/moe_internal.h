@@ -100,8 +100,10 @@ hipError_t launch_gemm(Elem e, Epi epi, const GemmArgs& a, const GemmPlan& p, hi
 GemmPlan plan_dense_splitk(int64_t T, int N, int K, int chunk);
 hipError_t launch_splitk_reduce(const GemmArgs& a, int ksplit, hipStream_t s);
 
-// --- activation quantisation (K4) -------------------------------------------
+// --- FP8: activation quantisation (K4) and block-scaled grouped GEMM ---------
 hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* q, float* scale, int64_t rows, int cols, hipStream_t s);
+GemmPlan plan_gemm_fp8(Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N);
+hipError_t launch_gemm_fp8(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
 
 // --- combine (K7) ------------------------------------------------------------
 struct CombineArgs {

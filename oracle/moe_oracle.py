@@ -193,7 +193,10 @@ def quantize_fp8_rows(v):
 
     a = max |v| over the block; a == 0 -> codes 0, scale 1; otherwise
     inv = 448 / a, q = e4m3_round(v * inv), scale = a / 448 (each a float32
-    operation). Returns (q as float64 values, scales float32 [rows, cols/128]).
+    operation). A block so small that 448 / a overflows float32 (a below
+    about 2**-119) takes the largest finite float32 as inv instead, so its
+    codes stay finite. Returns (q as float64 values, scales float32
+    [rows, cols/128]).
     """
     v = np.asarray(v, dtype=F32)
     rows, cols = v.shape
@@ -201,7 +204,9 @@ def quantize_fp8_rows(v):
     a = np.max(np.abs(blk), axis=2)
     nz = a > 0
     safe = np.where(nz, a, F32(1.0))
-    inv = (F32(448.0) / safe).astype(F32)
+    with np.errstate(over="ignore"):
+        inv = (F32(448.0) / safe).astype(F32)
+    inv = np.minimum(inv, F32(np.finfo(F32).max))   # a < 2**-119: 448 / a overflows
     prod = (blk * inv[:, :, None]).astype(F32)
     q = np.where(nz[:, :, None], e4m3_round(prod), 0.0)
     scale = np.where(nz, (safe / F32(448.0)).astype(F32), F32(1.0)).astype(F32)

@@ -2,7 +2,8 @@
 
 Routing ids and gates, counts, offsets, permutation and inverse permutation
 are compared bit for bit, with both sides given the same logits; layer
-outputs within max|dy| / RMS(y_oracle) <= 1e-5 (fp32), 2e-2 (bf16).
+outputs within max|dy| / RMS(y_oracle) <= 1e-5 (fp32), 2e-2 (bf16), 6e-2 (fp8).
+The fp8 activation quantiser is compared bit for bit (codes and scales).
 """
 import math
 
@@ -175,6 +176,12 @@ LAYER_CASES = {
     "small_bf16_gamma": lambda: _small(routed_scale=2.5, T=50, inter=384, shared_inter=128),
     "ep8_decode_bf16_T48": lambda: workload("ep8_decode_bf16", T=48),
     "full_decode_bf16_T40": lambda: workload("full_decode_bf16", T=40),
+    "small_fp8": lambda: _small(dtype="fp8", T=150, score_bias="zero"),
+    "small_fp8_capacity": lambda: _small(dtype="fp8", T=300, capacity_factor=1.25, router_bias="zipf1.1",
+                                         score_bias="zero"),
+    "small_fp8_share_wide": lambda: _small(dtype="fp8", T=90, expert_begin=8, expert_end=40, inter=384,
+                                           shared_inter=128, hidden=1024),
+    "fp8_skew_T96": lambda: workload("fp8_skew", T=96),
 }
 
 
@@ -220,6 +227,41 @@ def test_layer_stages_match_oracle(name):
     torch.cuda.synchronize()
     assert torch.equal(lo, r["logits"]) and torch.equal(io, r["ids"])
     assert torch.equal(y2, r["y"])
+
+
+# ---------------------------------------------------------------------------
+# FP8 activation quantiser: codes and scales bit for bit
+# ---------------------------------------------------------------------------
+
+def _quant_input(rows, H, rng):
+    x = rng.standard_normal((rows, H)).astype(F32)
+    if rows > 6:
+        x[0, :128] = 0.0                                  # all-zero block -> scale 1, zero codes
+        x[1, 128:256] = -0.0
+        x[2] *= 3.0e4                                     # large values
+        x[3] *= 1.0e-30                                   # tiny values (subnormal e4m3 codes)
+        x[4, 5] = 1.0e6                                   # one outlier per block
+        x[5, :] = np.tile(np.array([448.0, -448.0, 0.5, -0.25], F32), H // 4)
+        x[6, 128:256] = 2.0 ** -130                       # bf16 subnormals: 448 / amax overflows
+        x[6, 256 % H:256 % H + 128] = 2.0 ** -110             # small but normal
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("rows,H", [(1, 128), (37, 512), (300, 7168), (4099, 1024)])
+def test_quantize_fp8_bit_exact(rows, H):
+    say("quantize_fp8 case", rows, H)
+    cfg = moe.make_config(H, 8, 2, 128, dtype="fp8", n_group=1, topk_group=1, score_fn="softmax")
+    rng = np.random.default_rng(rows * 7 + H)
+    x = _quant_input(rows, H, rng)
+    q = torch.full((rows, H), 0xAA, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(rows, H // 128, dtype=torch.float32, device="cuda")
+    moe.moe_quantize_fp8(cfg, x.cuda(), q, sc)
+    torch.cuda.synchronize()
+    want_q, want_s = O.quantize_fp8_rows(x.float().numpy())
+    got_q = q.cpu().numpy()
+    assert np.array_equal(host(sc).view(np.int32), want_s.view(np.int32))
+    assert not np.any((got_q & 0x7F) == 0x7F)             # no NaN codes
+    assert np.array_equal(O.e4m3_decode(got_q), want_q)
 
 
 def test_bf16_output_dtype():

@@ -126,6 +126,29 @@ def test_quantize_fp8_rows_invariants():
     assert np.all(err <= np.maximum(np.abs(v) * 2.0 ** -4, (s.repeat(128, axis=1)) * 2.0 ** -10) + 1e-12)
 
 
+def test_quantize_fp8_rows_matches_torch_cast_and_tiny_blocks():
+    """Ordinary blocks: the codes are torch's own float8_e4m3fn cast of the
+    float32 product v * (448 / a) (an independent RNE implementation); a
+    block whose 448 / a overflows float32 keeps finite codes."""
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((8, 256)).astype(F32) * rng.uniform(1e-3, 1e3, (8, 1)).astype(F32)
+    q, s = O.quantize_fp8_rows(v)
+    a = np.max(np.abs(v.reshape(8, 2, 128)), axis=2)
+    inv = torch.from_numpy(np.full_like(a, 448.0)) / torch.from_numpy(a)
+    prod = torch.from_numpy(v.reshape(8, 2, 128)) * inv[:, :, None]
+    want = prod.to(torch.float8_e4m3fn).double().reshape(8, 256).numpy()
+    assert np.array_equal(q, want)
+    assert np.array_equal(s, (torch.from_numpy(a) / 448.0).numpy())
+    tiny = np.zeros((1, 128), F32)
+    tiny[0, :] = F32(2.0 ** -130)
+    tiny[0, 1] = F32(-(2.0 ** -131))
+    qt, st = O.quantize_fp8_rows(tiny)
+    assert np.all(np.isfinite(qt)) and np.all(np.abs(qt) <= 448.0)
+    # inv = largest float32 ~ 2**128: 2**-130 -> 0.25, -2**-131 -> -0.125
+    assert qt[0, 0] == 0.25 and qt[0, 1] == -0.125
+    assert st[0, 0] == F32(2.0 ** -130) / F32(448.0)
+
+
 def test_block_weight_dequant_matches_torch():
     rng = np.random.default_rng(4)
     codes = rng.integers(0, 256, (256, 384), dtype=np.uint8)
