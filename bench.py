@@ -9,8 +9,10 @@ dominant kernel (measured with HIP events over the timed steps) and the CPU
 oracle timed on a bounded sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,9 +35,57 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="ep8_decode_bf16")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
-    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens of the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the layer, run a plain device copy of MIB MiB 5 times (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return ap.parse_args()
+
+
+# Kernel sources whose code a stored traffic measurement belongs to.
+KERNEL_SOURCES = {"bf16": ["gemm.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
+                  "f32": ["gemm.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
+                  "fp8": ["gemm_fp8.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"]}
+
+
+def kernel_source_hash(dtype):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[dtype]:
+        with open(os.path.join(ROOT, "mixture_experts_layer_10_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(stage, workload, dtype):
+    """HBM bytes per launch of `stage` from the committed counter summary
+    (profiles/<stage>_<workload>_hbm_traffic.md), or None when there is none
+    or the kernel's sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        text = fh.read()
+    m = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    hsh = re.search(r"^kernel_source_sha256:\s*([0-9a-f]+)", text, re.M)
+    if not m or not hsh or hsh.group(1) != kernel_source_hash(dtype):
+        return None
+    return float(m.group(1))
+
+
+def calibrate_copy(mib):
+    """A plain copy kernel of known size: dst = src * 1 over `mib` MiB of
+    float32, five times; each launch reads and writes exactly mib MiB."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4,
+                      "launches": 5}), flush=True)
 
 
 def stage_bytes_flops(w, counts, stage):
@@ -59,9 +109,11 @@ def stage_bytes_flops(w, counts, stage):
     raise ValueError(stage)
 
 
-def cpu_baseline(w, inp, sample):
-    """The oracle as it stands, timed on the first `sample` tokens."""
+def cpu_baseline(w, inp, sample, min_seconds=10.0):
+    """The oracle as it stands, timed on the first `sample` tokens of the
+    batch, in passes repeated until at least `min_seconds` have elapsed."""
     import platform
+    import torch
     from oracle import moe_oracle as O
 
     try:
@@ -74,8 +126,7 @@ def cpu_baseline(w, inp, sample):
         if t is None:
             return None
         t = t.detach().cpu()
-        return t.float().numpy() if t.dtype.is_floating_point and t.dtype != __import__("torch").float8_e4m3fn \
-            else t.view(__import__("torch").uint8).numpy()
+        return t.view(torch.uint8).numpy() if t.dtype == torch.float8_e4m3fn else t.float().numpy()
 
     cfg = O.Config.from_workload(w)
     S = min(sample, w["T"])
@@ -84,13 +135,18 @@ def cpu_baseline(w, inp, sample):
                 shared_w13=h(inp["shared_w13"]), shared_w2=h(inp["shared_w2"]))
     scales = {k: h(inp.get(k)) for k in ("w13_scale", "w2_scale", "shared_w13_scale", "shared_w2_scale")}
     wr, w13, w2 = h(inp["w_router"]), h(inp["w13"]), h(inp["w2"])
+    passes = 0
     t0 = time.perf_counter()
-    O.forward(cfg, x, wr, w13, w2, scales=scales, **args)
-    dt = time.perf_counter() - t0
+    while True:
+        O.forward(cfg, x, wr, w13, w2, scales=scales, **args)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     cores = len(os.sched_getaffinity(0))
-    return {"value": S / dt, "unit": "tokens/s", "cores": blas_threads or cores, "kind": "oracle",
-            "sample": f"first {S} of {w['T']} tokens of the same workload, whole layer "
-                      f"(route, dispatch, experts, shared expert, combine), {dt:.1f} s wall",
+    return {"value": passes * S / dt, "unit": "tokens/s", "cores": blas_threads or cores, "kind": "oracle",
+            "sample": f"first {S} of {w['T']} tokens of the same workload, whole layer (router GEMM, top-k, "
+                      f"dispatch, experts, shared expert, combine), {passes} passes in {dt:.1f} s wall",
             "affinity_cores": cores, "cpu": platform.processor() or platform.machine()}
 
 
@@ -100,6 +156,9 @@ def main():
         print(f"bench.py runs on one GPU: --gpus {a.gpus} is not supported by this build "
               "(the layer runs one GPU's share of experts; no collectives).", file=sys.stderr)
         sys.exit(2)
+    if a.calibrate_copy:
+        calibrate_copy(a.calibrate_copy)
+        return
     import torch
     import mixture_experts_layer_10_amd as moe
     from synth import make_inputs, workload
@@ -158,7 +217,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": peak_mfma, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = stored_traffic(dom, a.config, w["dtype"])
     roof["kernel"] = f"gemm_kernel ({dom})"
     roof["kernel_ms"] = stage_ms[dom]
     roof["algorithmic_bytes"] = byts
