@@ -40,6 +40,7 @@
 #include <float.h>
 
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 #include <utility>
 
@@ -142,8 +143,9 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
     for (int f = 0; f < 4; ++f) {
         int brow;
         if constexpr (EPI == Epi::SWIGLU) {
-            const int n0 = nt * HC + wave * 32;
-            brow = (f < 2) ? n0 + 16 * f + lr : a.inter + n0 + 16 * (f - 2) + lr;
+            int col = nt * HC + wave * 32 + 16 * (f & 1) + lr;
+            col = col < a.inter ? col : a.inter - 1;   // column tail: valid row, result dropped
+            brow = (f < 2) ? col : a.inter + col;
         } else {
             brow = nt * PC + wave * 64 + 16 * f + lr;
             brow = brow < a.N ? brow : a.N - 1;        // column tail: valid row, result dropped
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int r = i * 16 + lq * 4 + v;
-                        if (r < rows) {
+                        if (r < rows && col < a.N) {
                             const float h = silu_mul(acc[i][f][v], acc[i][f + 2][v]);
                             const int64_t off = (crow0 + r) * a.ldc + col;
                             if constexpr (EL == Elem::F32)
@@ -460,15 +462,24 @@ hipError_t launch_bm(GemmArgs a, const GemmPlan& p, hipStream_t s) {
     a.ksplit = p.ksplit < 1 ? 1 : p.ksplit;
     if (p.nw == 8) {
         if constexpr (EL == Elem::BF16) {
-            if (p.bm != 128) return hipErrorInvalidValue;
-            launch_one<EL, EPI, 128, 1, 1, true, false, 8>(a, p, s);
+            if (p.smajor && p.bm == 128) launch_one<EL, EPI, 128, 1, 1, true, false, 8>(a, p, s);
+            else if (p.smajor && p.bm == 96) launch_one<EL, EPI, 96, 1, 1, true, false, 8>(a, p, s);
+            else if (!p.smajor && p.bm == 32) launch_one<EL, EPI, 32, 1, 2, false, false, 8>(a, p, s);
+            else return hipErrorInvalidValue;
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
     }
+    if (p.smajor) return hipErrorInvalidValue;
     switch (p.bm) {
         case 32: launch_one<EL, EPI, 32, 1, 2>(a, p, s); break;
-        case 64: launch_one<EL, EPI, 64, (EL == Elem::F32 ? 1 : 2), 2>(a, p, s); break;
+        case 64: launch_one<EL, EPI, 64, 1, 2>(a, p, s); break;
+        case 96:
+            if constexpr (EL == Elem::BF16) {
+                launch_one<EL, EPI, 96, 1, 2>(a, p, s);
+                break;
+            }
+            return hipErrorInvalidValue;
         case 128: launch_one<EL, EPI, 128, 1, 2>(a, p, s); break;
         case 192:
             if constexpr (EL == Elem::BF16) {
@@ -486,16 +497,38 @@ hipError_t launch_bm(GemmArgs a, const GemmPlan& p, hipStream_t s) {
 GemmPlan plan_gemm(Elem e, Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N) {
     GemmPlan p;
     p.nw = 4;
+    p.smajor = 0;
+    p.big = 0;
     p.ksplit = 1;
-    p.bm = expected_rows_per_group <= 32 ? 32 : expected_rows_per_group <= 64 ? 64 : 128;
     auto cols = [&](int nw) { return (epi == Epi::SWIGLU ? 32 : 64) * nw; };
-    // Compute-bound shapes: 128-row tiles on 8 wavefronts (two per SIMD)
-    // when that still gives every CU a couple of workgroups.
-    if (e == Elem::BF16 && expected_rows_per_group >= 128) {
-        const int64_t blocks8 = (rows_upper / 128) * ((N + cols(8) - 1) / cols(8));
-        if (blocks8 >= 512) {
-            p.bm = 128;
+    const double m = static_cast<double>(expected_rows_per_group);
+    // Hundreds of rows per group and enough tiles to fill the GPU: 256 x 256
+    // tiles through the LDS pipeline of gemm_big.hip.
+    if (e == Elem::BF16 && m >= 256) {
+        const GemmPlan big = plan_gemm_big(epi, rows_upper, n_groups, N);
+        if ((rows_upper / 256) * big.n_tiles >= 512) return big;
+    }
+    if (m >= 128) {
+        // Compute-bound shapes: 128-row tiles; on 8 wavefronts (two per SIMD,
+        // weights consumed sub-run by sub-run) when that still gives every CU
+        // a couple of workgroups.
+        p.bm = 128;
+        if (e == Elem::BF16 && (epi == Epi::PLAIN || N % cols(8) == 0) &&
+            (rows_upper / 128) * ((N + cols(8) - 1) / cols(8)) >= 512) {
             p.nw = 8;
+            p.smajor = 1;
+        }
+    } else {
+        // Bandwidth-bound shapes: one m-tile should cover nearly every group
+        // (the expected count plus three standard deviations of a Poisson
+        // count), because a second m-tile streams the same weights again.
+        const double need = m + 3.0 * std::sqrt(m);
+        p.bm = need <= 32 ? 32 : need <= 64 ? 64 : (need <= 96 && e == Elem::BF16) ? 96 : 128;
+        // two wavefronts per SIMD (for SwiGLU only when 8 x 32 h columns tile N)
+        if (e == Elem::BF16 && p.bm == 32 && (epi == Epi::PLAIN || N % cols(8) == 0)) p.nw = 8;
+        if (e == Elem::BF16 && p.bm == 96 && epi == Epi::PLAIN) {
+            p.nw = 8;
+            p.smajor = 1;
         }
     }
     p.n_tiles = (N + cols(p.nw) - 1) / cols(p.nw);
@@ -508,6 +541,8 @@ GemmPlan plan_gemm(Elem e, Epi epi, int64_t rows_upper, int n_groups, int64_t ex
 GemmPlan plan_dense_splitk(int64_t T, int N, int K, int chunk) {
     GemmPlan p;
     p.nw = 4;
+    p.smajor = 0;
+    p.big = 0;
     p.bm = T <= 32 ? 32 : T <= 1024 ? 64 : 128;
     p.n_tiles = (N + 255) / 256;
     const int64_t tiles = (T + p.bm - 1) / p.bm * p.n_tiles;
@@ -535,6 +570,7 @@ hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_
 
 hipError_t launch_gemm(Elem e, Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     if (p.grid == 0) return hipSuccess;
+    if (p.big) return e == Elem::BF16 ? launch_gemm_big(epi, a, p, s) : hipErrorInvalidValue;
     if (e == Elem::BF16)
         return epi == Epi::SWIGLU ? launch_bm<Elem::BF16, Epi::SWIGLU>(a, p, s) : launch_bm<Elem::BF16, Epi::PLAIN>(a, p, s);
     if (e == Elem::F32)

@@ -1,0 +1,302 @@
+// K5 / K6 at compute-bound shapes (bf16): grouped GEMM with 256 x 256 tiles
+// staged through LDS (double-buffered) by direct global -> LDS loads.
+//
+// What it computes is that of gemm.hip (Perplexity "Lower latency and higher
+// throughput with multi-node DeepSeek deployment", section "Roofline >
+// GroupGEMM": per group, rows x weight^T; SWIGLU epilogue h = silu(gate) * up,
+// infra guide "Data parallelism and expert parallelism", section 2.1). This
+// variant is for groups of hundreds of rows (prefill), where the product is
+// bound by matrix throughput rather than by streaming the weights once:
+//
+//  * a workgroup computes 256 rows x 256 weight rows; its NW wavefronts
+//    (8 by default, two per SIMD; 4 also built) form 2 x NW/2 and each
+//    computes 128 rows x 512/NW weight rows as 32 x 32 fragments of
+//    v_mfma_f32_32x32x16_bf16;
+//  * both operands go HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR
+//    staging), K = 64 per stage: each row's 128 bytes are one whole cache
+//    line, so a load instruction touches 8 lines (half-line loads, 16 rows of
+//    64 bytes, ran about a third slower); two stages (128 KB);
+//  * one barrier per stage, placed mid-stage: the MFMAs of a stage's last two
+//    k-steps run while the next stage's first fragments are read and the
+//    stage after next is loaded;
+//  * 16-byte granule q of LDS row r sits at q ^ ((r >> 1) & 7), which makes
+//    the fragment reads (32 rows x one granule per lane half) free of bank
+//    conflicts (measured with the bank-conflict counter); the direct loads
+//    fill 8 rows per instruction, lane l taking the granule that the swizzle
+//    puts at its position;
+//  * SwiGLU tiles interleave gate and up rows so that each wavefront holds
+//    matching gate and up columns: h = silu(g) * u is formed in registers;
+//  * a group's rows are split evenly over its m-tiles, and 32-row blocks past
+//    a tile's real row count skip their MFMAs.
+#include <utility>
+
+#include "gemm_tile.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBM = 256;                  // rows per tile
+constexpr int kBN = 256;                  // weight rows per tile
+constexpr int kKB = 64;                   // K per stage
+constexpr int kRowB = kKB * 2;            // 128 LDS bytes per row per stage: whole cache lines
+constexpr int kGran = kRowB / 16;         // 16-byte granules per row
+constexpr int kStages = 2;
+constexpr int kStageB = (kBM + kBN) * kRowB;   // 64 KB
+
+// LDS swizzle: granule q of row r sits at q ^ ((r >> 1) & 7).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ bf16x8 lds_frag(const unsigned char* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const vec16*>(p));
+}
+
+__device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ float silu_mul_big(float g, float u) {
+    return g / (1.0f + __expf(-g)) * u;
+}
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]).
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+// NW wavefronts as 2 (rows) x NW/2 (columns); each computes 128 rows x
+// WB = 512 / NW weight rows. With NW = 8 two wavefronts share each SIMD, so
+// one issues MFMAs while the other waits at a barrier or on LDS.
+template <Epi EPI, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_tiles) {
+    constexpr int NT = NW * 64;
+    constexpr int WB = 2 * kBN / NW;                 // weight rows per wavefront
+    constexpr int NJ = WB / 32;                      // 32-column fragments per wavefront
+    constexpr int kLoads = kBM * kGran / NT;         // direct loads per thread per operand per stage
+    constexpr int kRowsPerLoad = 64 / kGran;         // rows one direct load fills (1 KB)
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_ring[];   // kStages x kStageB
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // wave-uniform (scalar branches)
+    const int wm = wave & 1, wn = wave >> 1;
+
+    Tile tl;
+    if (!find_tile(a, n_tiles, kBM, tl, /*balanced=*/true)) return;
+    const int g = tl.g, nt = tl.nt;
+    const bool shared = tl.shared;
+    const int row0 = tl.row0, m0 = tl.m0, rows = tl.rows;
+    const int K = a.K;
+    const int nkb = K / kKB;
+    const int last = nkb - 1;
+
+    // ---- direct-load sources: instruction j of wavefront w fills rows
+    // (NW j + w) * 8 + lane / 8 of the stage, granule slot lane % 8, and
+    // loads the granule the swizzle places there --------------------------
+    const int lrow = lane / kGran;                                 // row within the instruction's rows
+    auto slot_granule = [&](int row) { return (lane % kGran) ^ swz(row); };
+    const unsigned char* Ag = static_cast<const unsigned char*>(shared ? a.A_shared : a.A);
+    uint32_t aoff[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int rs = (NW * j + wave) * kRowsPerLoad + lrow;
+        const int r = rs < rows ? rs : rows - 1;                    // rows past the end: a valid row, unused
+        uint32_t src;
+        if (shared) src = m0 + r;
+        else if (a.gather) src = static_cast<uint32_t>(a.perm[row0 + m0 + r] / a.topk);
+        else src = row0 + m0 + r;
+        aoff[j] = src * static_cast<uint32_t>(K * 2) + slot_granule(rs) * 16;
+    }
+    const unsigned char* Bg = shared ? static_cast<const unsigned char*>(a.B_shared)
+                                     : static_cast<const unsigned char*>(a.B) + static_cast<int64_t>(g) * a.b_stride * 2;
+    uint32_t boff[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int n = (NW * j + wave) * kRowsPerLoad + lrow;       // weight row slot of the tile
+        int brow;
+        if constexpr (EPI == Epi::SWIGLU) {
+            // slots [WB wn, WB wn + WB): WB/2 gate rows then the WB/2 up rows
+            // of the same h columns
+            int col = nt * 128 + (n / WB) * (WB / 2) + (n % (WB / 2));
+            col = col < a.inter ? col : a.inter - 1;                // column tail: valid row, result dropped
+            brow = (n & (WB / 2)) ? a.inter + col : col;
+        } else {
+            brow = nt * kBN + n;
+            brow = brow < a.N ? brow : a.N - 1;
+        }
+        boff[j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + slot_granule(n) * 16;
+    }
+    auto issue = [&](int kb, int stage) __attribute__((always_inline)) {
+        unsigned char* sa = s_ring + stage * kStageB;
+        unsigned char* sb = sa + kBM * kRowB;
+        const uint32_t ko = static_cast<uint32_t>(kb) * kRowB;
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) load_lds16(Ag + aoff[j] + ko, sa + (NW * j + wave) * kRowsPerLoad * kRowB);
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) load_lds16(Bg + boff[j] + ko, sb + (NW * j + wave) * kRowsPerLoad * kRowB);
+    };
+
+    // ---- fragment reads: lane l reads row (l % 32) of a 32-row block,
+    // granule 2t + l / 32 of k-step t ------------------------------------------
+    constexpr int KSTEPS = kKB / 16;
+    const int fr = lane & 31;
+    int f_off[KSTEPS];
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) f_off[t] = fr * kRowB + (((2 * t + (lane >> 5)) ^ swz(fr)) * 16);
+    const int a_base = wm * 128 * kRowB;
+    const int b_base = kBM * kRowB + wn * WB * kRowB;
+    const int nrb = (rows + 31) >> 5;                               // 32-row blocks with data
+
+    f32x16 acc[4][NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+
+    // Rows blocks of this wavefront that hold data (uniform: scalar branches).
+    const int nbw = min(max(nrb - wm * 4, 0), 4);
+    // Fragments of k-steps 0..3 of a stage (4 x (4 A + NJ B) registers).
+    bf16x8 af[KSTEPS][4], bfr[KSTEPS][NJ];
+    auto read = [&](int slot, int t) __attribute__((always_inline)) {
+        const unsigned char* st = s_ring + slot * kStageB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[t][i] = lds_frag(st + a_base + i * 32 * kRowB + f_off[t]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bfr[t][j] = lds_frag(st + b_base + j * 32 * kRowB + f_off[t]);
+    };
+    auto mfma = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < nbw) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t][i], bfr[t][j], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+    // Wait for this thread's LDS fills and LDS reads, then a bare barrier
+    // (no fence: the fills are waited for explicitly). The empty asm
+    // statements keep the compiler from moving memory accesses across it,
+    // the scheduling barriers keep MFMAs on their side of it.
+    auto sync = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- pipeline (two LDS slots) -------------------------------------------
+    // Iteration kb: MFMAs of k-steps 0-1 of stage kb while its k-steps 2-3 are
+    // read; then one barrier (stage kb+1 has landed everywhere, no one reads
+    // stage kb's slot any more); then the loads of stage kb+2 into that slot
+    // and the reads of stage kb+1's first k-steps are issued while k-steps 2-3
+    // of stage kb run. Loads are unconditional (indices clamped), so the
+    // waits are exact; nothing past the last stage is used.
+    issue(0, 0);
+    sync();
+    issue(min(1, last), 1);
+    read(0, 0);
+    read(0, 1);
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int s = kb & 1;
+        read(s, 2);
+        mfma(0);
+        read(s, 3);
+        mfma(1);
+        sync();
+        issue(min(kb + 2, last), s);
+        read(s ^ 1, 0);
+        read(s ^ 1, 1);
+        mfma(2);
+        mfma(3);
+    }
+    // The clamped last loads are still landing: no direct-load write may
+    // outlive the workgroup's LDS allocation.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+
+    // ---- epilogue: lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32)
+    // + e % 4 of each 32 x 32 fragment -----------------------------------------
+    const int64_t crow0 = shared ? m0 : static_cast<int64_t>(row0) + m0;
+    unsigned char* Cb = static_cast<unsigned char*>(shared ? a.C_shared : a.C);
+    const int lc = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (wm * 4 + i < nrb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = wm * 128 + i * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+                if (r < rows) {
+                    const int64_t rb = (crow0 + r) * a.ldc;
+                    if constexpr (EPI == Epi::SWIGLU) {
+#pragma unroll
+                        for (int j = 0; j < NJ / 2; ++j) {
+                            const int col = nt * 128 + wn * (WB / 2) + j * 32 + lc;
+                            if (col < a.N)
+                                reinterpret_cast<uint16_t*>(Cb)[rb + col] =
+                                    f32_to_bf16_bits(silu_mul_big(acc[i][j][e], acc[i][j + NJ / 2][e]));
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j) {
+                            const int col = nt * kBN + wn * WB + j * 32 + lc;
+                            if (col < a.N) {
+                                if (a.out_f32)
+                                    reinterpret_cast<float*>(Cb)[rb + col] = acc[i][j][e];
+                                else
+                                    reinterpret_cast<uint16_t*>(Cb)[rb + col] = f32_to_bf16_bits(acc[i][j][e]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <Epi EPI, int NW>
+hipError_t launch_big_epi(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    constexpr int lds = kStages * kStageB;
+    static bool attr_set = false;              // once per instantiation
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<EPI, NW>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((gemm_big_kernel<EPI, NW>), dim3(static_cast<unsigned>(p.grid)), dim3(NW * 64), lds, s, a,
+                       p.n_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Plan of the 256 x 256 tile kernel: n_tiles column tiles (128 h columns for
+// SWIGLU, 256 output columns for PLAIN), grid an upper bound on the tiles.
+GemmPlan plan_gemm_big(Epi epi, int64_t rows_upper, int n_groups, int N) {
+    GemmPlan p;
+    p.bm = kBM;
+    p.nw = 8;
+    p.smajor = 0;
+    p.ksplit = 1;
+    p.big = 1;
+    const int cols = epi == Epi::SWIGLU ? 128 : kBN;
+    p.n_tiles = (N + cols - 1) / cols;
+    const int64_t m_tiles = rows_upper / kBM + n_groups;
+    p.grid = ((m_tiles * p.n_tiles + 7) / 8) * 8;
+    return p;
+}
+
+hipError_t launch_gemm_big(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    if (p.grid == 0) return hipSuccess;
+    if (a.K % kKB != 0) return hipErrorInvalidValue;
+    GemmArgs b = a;
+    b.ksplit = 1;
+    if (p.nw == 8)
+        return epi == Epi::SWIGLU ? launch_big_epi<Epi::SWIGLU, 8>(b, p, s) : launch_big_epi<Epi::PLAIN, 8>(b, p, s);
+    if (p.nw == 4)
+        return epi == Epi::SWIGLU ? launch_big_epi<Epi::SWIGLU, 4>(b, p, s) : launch_big_epi<Epi::PLAIN, 4>(b, p, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

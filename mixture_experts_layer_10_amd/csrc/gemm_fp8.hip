@@ -338,6 +338,8 @@ hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* q, float* scale, int64_
 GemmPlan plan_gemm_fp8(Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N) {
     GemmPlan p;
     p.nw = 4;
+    p.smajor = 0;
+    p.big = 0;
     p.ksplit = 1;
     p.bm = expected_rows_per_group <= 32 ? 32 : expected_rows_per_group <= 64 ? 64 : 128;
     const int cols = epi == Epi::SWIGLU ? 128 : 256;

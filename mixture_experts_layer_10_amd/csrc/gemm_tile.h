@@ -23,7 +23,12 @@ struct Tile {
 // L2. Group row counts come from device memory (dispatch offsets and the
 // m-tile schedule), never from the host. Returns false for workgroups past
 // the last item (the grid is an upper bound). Uniform across the workgroup.
-__device__ __forceinline__ bool find_tile(const GemmArgs& a, int n_tiles, int BM, Tile& t) {
+//
+// With `balanced`, a group's rows are split into its m-tiles evenly (each
+// tile a multiple of 32 rows, at most BM) instead of BM, BM, ..., remainder:
+// the m-tile count is the same, but no tile is left with a sliver of rows
+// that still streams the whole weight panel.
+__device__ __forceinline__ bool find_tile(const GemmArgs& a, int n_tiles, int BM, Tile& t, bool balanced = false) {
     const int KS = a.ksplit;
     const int n_groups = a.n_local + a.has_shared;
     const int per_item = n_tiles * KS;                 // items per m-tile
@@ -57,8 +62,13 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& a, int n_tiles, int BM
         t.row0 = a.offsets[g];
         rows_g = a.offsets[g + 1] - t.row0;
     }
-    t.m0 = mt * BM;
-    t.rows = min(BM, rows_g - t.m0);
+    int tr = BM;
+    if (balanced) {
+        tr = (rows_g + mt_count - 1) / mt_count;
+        tr = min(BM, (tr + 31) & ~31);
+    }
+    t.m0 = mt * tr;
+    t.rows = min(tr, rows_g - t.m0);
     return true;
 }
 

@@ -290,11 +290,17 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
     g2.ldc = static_cast<int>(H);
     g2.out_f32 = c->dtype == MOE_DTYPE_F32;
     GemmPlan p2 = plan_gemm(el, Epi::PLAIN, P, El, per_expert, static_cast<int>(H));
-    if (p2.bm != p1.bm) {    // the down GEMM reuses the gate/up schedule's m-tiles
-        p2.bm = p1.bm;
-        p2.nw = p1.nw;
-        p2.n_tiles = (static_cast<int>(H) + 64 * p2.nw - 1) / (64 * p2.nw);
-        p2.grid = ((P / p2.bm + El) * p2.n_tiles + 7) / 8 * 8;
+    if (p2.bm != p1.bm || p2.big != p1.big) {    // the down GEMM reuses the gate/up schedule's m-tiles
+        if (p1.big) {
+            p2 = plan_gemm_big(Epi::PLAIN, P, El, static_cast<int>(H));
+        } else {
+            p2.big = 0;
+            p2.bm = p1.bm;
+            p2.nw = p1.nw;
+            p2.smajor = p1.smajor;
+            p2.n_tiles = (static_cast<int>(H) + 64 * p2.nw - 1) / (64 * p2.nw);
+            p2.grid = ((P / p2.bm + El) * p2.n_tiles + 7) / 8 * 8;
+        }
     }
     StageTimer tm(MOE_STAGE_DOWN, s);
     return launch_gemm(el, Epi::PLAIN, g2, p2, s);

@@ -87,6 +87,8 @@ struct GemmArgs {
 struct GemmPlan {
     int bm;                   // rows per tile
     int nw;                   // wavefronts per workgroup (4 or 8)
+    int smajor;               // weights consumed sub-run by sub-run (one register buffer)
+    int big;                  // 256 x 256 LDS-pipelined tiles (gemm_big.hip)
     int n_tiles;              // column tiles per group
     int ksplit;               // K slices per tile
     int64_t grid;             // workgroups launched (upper bound on tiles * ksplit)
@@ -99,6 +101,9 @@ hipError_t launch_gemm(Elem e, Epi epi, const GemmArgs& a, const GemmPlan& p, hi
 // max_split * T * N floats.
 GemmPlan plan_dense_splitk(int64_t T, int N, int K, int chunk);
 hipError_t launch_splitk_reduce(const GemmArgs& a, int ksplit, hipStream_t s);
+// Compute-bound shapes (bf16): 256 x 256 tiles through a 4-stage LDS ring.
+GemmPlan plan_gemm_big(Epi epi, int64_t rows_upper, int n_groups, int N);
+hipError_t launch_gemm_big(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
 
 // --- FP8: activation quantisation (K4) and block-scaled grouped GEMM ---------
 hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* q, float* scale, int64_t rows, int cols, hipStream_t s);

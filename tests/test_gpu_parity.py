@@ -176,6 +176,16 @@ LAYER_CASES = {
     "small_bf16_gamma": lambda: _small(routed_scale=2.5, T=50, inter=384, shared_inter=128),
     "ep8_decode_bf16_T48": lambda: workload("ep8_decode_bf16", T=48),
     "full_decode_bf16_T40": lambda: workload("full_decode_bf16", T=40),
+    # tile shapes: 64-, 96- and 128-row decode tiles, and the 8-wavefront
+    # 128 x 512 prefill tile (expected rows per expert 28, 66, 113, 128)
+    "small_bf16_bm64": lambda: _small(T=300),
+    "small_bf16_bm96": lambda: _small(T=700),
+    "small_bf16_bm128": lambda: _small(T=1200),
+    "small_bf16_prefill_tiles": lambda: _small(T=1366, inter=2048, shared_inter=256, score_bias="zero"),
+    # 256 x 256 LDS-pipelined tiles (about 256 rows per expert, 8192 rows):
+    # gate/up on them, the down GEMM following its schedule
+    "small_bf16_big_tiles": lambda: _small(T=2048, n_experts=32, expert_end=32, top_k=4, n_group=4, topk_group=2,
+                                           inter=2048, shared_inter=2048, score_bias="zero"),
     "small_fp8": lambda: _small(dtype="fp8", T=150, score_bias="zero"),
     "small_fp8_capacity": lambda: _small(dtype="fp8", T=300, capacity_factor=1.25, router_bias="zipf1.1",
                                          score_bias="zero"),
