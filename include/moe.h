@@ -223,9 +223,12 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
  * starts recording: from then on every stage of every call records a start
  * and a stop event on its stream (at most n stages are recorded; later ones
  * are not). moe_profile_enable(0) stops and destroys the events;
- * moe_profile_reset() forgets what was recorded. moe_profile_query(stage)
- * waits for the recorded events of that stage and returns their summed
- * elapsed time and how many were recorded. Single-threaded use only. */
+ * moe_profile_reset() forgets what was recorded. moe_profile_select(mask)
+ * limits recording to the stages whose bit is set (bit s: stage s; all by
+ * default, kept across enable calls), so that a timed run can time one
+ * kernel without events around the others. moe_profile_query(stage) waits
+ * for the recorded events of that stage and returns their summed elapsed
+ * time and how many were recorded. Single-threaded use only. */
 enum moe_stage {
     MOE_STAGE_ROUTER_GEMM = 0,
     MOE_STAGE_ROUTE = 1,
@@ -240,6 +243,7 @@ enum moe_stage {
 };
 int moe_profile_enable(int max_records);
 int moe_profile_reset(void);
+int moe_profile_select(unsigned stage_mask);
 int moe_profile_query(int stage, double* total_ms, int* count);
 
 #ifdef __cplusplus

@@ -8,5 +8,5 @@ from .binding import (  # noqa: F401
     validate_config, workspace_bytes, workspace, make_weights, moe_router_gemm, moe_route,
     moe_dispatch, moe_expert_ffn, moe_combine, moe_forward, moe_quantize_fp8, LIB_PATH,
     SCORE_SOFTMAX, SCORE_SIGMOID, DTYPE_F32, DTYPE_BF16, DTYPE_FP8,
-    STAGES, profile_enable, profile_reset, profile_query,
+    STAGES, profile_enable, profile_reset, profile_query, profile_select,
 )

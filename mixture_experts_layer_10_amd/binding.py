@@ -73,6 +73,7 @@ def lib():
             "moe_quantize_fp8": (ctypes.c_int, [cfgp, i64, vp, vp, fp, vp]),
             "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
             "moe_profile_reset": (ctypes.c_int, []),
+            "moe_profile_select": (ctypes.c_int, [ctypes.c_uint]),
             "moe_profile_query": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                                   ctypes.POINTER(ctypes.c_int)]),
         }
@@ -304,6 +305,12 @@ def profile_enable(max_records):
 
 def profile_reset():
     _check(lib().moe_profile_reset(), "moe_profile_reset")
+
+
+def profile_select(stages=None):
+    """Record only the named stages (None: all)."""
+    mask = 0xFFFFFFFF if stages is None else sum(1 << STAGES.index(n) for n in stages)
+    _check(lib().moe_profile_select(mask), "moe_profile_select")
 
 
 def profile_query():

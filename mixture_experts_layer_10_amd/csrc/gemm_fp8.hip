@@ -101,11 +101,12 @@ __global__ __launch_bounds__(kThreads, (BM <= 32 ? 2 : 1)) void gemm_fp8_kernel(
     __shared__ __attribute__((aligned(16))) float s_sa[2][BM];      // activation scales of the chunk
     __shared__ float s_amax[4][BM];                                 // SwiGLU epilogue: per-wave row amax
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // wave-uniform: scalar scale loads
     const int lr = lane & 15, lq = lane >> 4;
 
     Tile tl;
-    if (!find_tile(a, n_tiles, BM, tl)) return;
+    if (!find_tile(a, n_tiles, BM, tl, /*balanced=*/true)) return;
     const int g = tl.g, nt = tl.nt;
     const bool shared = tl.shared;
     const int row0 = tl.row0, m0 = tl.m0, rows = tl.rows;
@@ -120,7 +121,6 @@ __global__ __launch_bounds__(kThreads, (BM <= 32 ? 2 : 1)) void gemm_fp8_kernel(
                                      : static_cast<const unsigned char*>(a.B) + static_cast<int64_t>(g) * a.b_stride;
     const float* Sg = shared ? a.B_scale_shared : a.B_scale + static_cast<int64_t>(g) * nb_rows * kblocks;
     uint32_t boff[4];
-    const float* bsc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
         int brow;
@@ -132,7 +132,19 @@ __global__ __launch_bounds__(kThreads, (BM <= 32 ? 2 : 1)) void gemm_fp8_kernel(
             brow = brow < a.N ? brow : a.N - 1;
         }
         boff[f] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K) + lq * 16;
-        bsc[f] = Sg + (brow / 128) * kblocks;          // 16 rows of a fragment share a 128-row block
+    }
+    // A wavefront's weight rows lie in one 128-row scale block per group
+    // (SWIGLU: the gate rows and the up rows, fragments 0-1 and 2-3; PLAIN:
+    // all four fragments): its weight scales are wave-uniform, one scalar
+    // load per group and chunk.
+    constexpr int NG = EPI == Epi::SWIGLU ? 2 : 1;
+    const float* bsc[NG];
+    if constexpr (EPI == Epi::SWIGLU) {
+        bsc[0] = Sg + nt * kblocks;
+        bsc[1] = Sg + (a.inter / 128 + nt) * kblocks;
+    } else {
+        const int blk = min((nt * 256 + wave * 64) / 128, a.N / 128 - 1);
+        bsc[0] = Sg + blk * kblocks;
     }
 
     // ---- activations: gathered e4m3 rows and their per-block scales --------
@@ -162,18 +174,19 @@ __global__ __launch_bounds__(kThreads, (BM <= 32 ? 2 : 1)) void gemm_fp8_kernel(
         for (int f = 0; f < 4; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     i32x8v breg[NB][4];
-    float bsreg[NB][4];
+    float bsreg[NB][NG];
     vec16 areg[APD][PASSES];
     float sareg[APD];
     const int last = nch - 1;
 
-    auto load_b = [&](i32x8v (&dst)[4], float (&ds)[4], int c) __attribute__((always_inline)) {
+    auto load_b = [&](i32x8v (&dst)[4], float (&ds)[NG], int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
             const unsigned char* p = Bg + boff[f] + static_cast<int64_t>(c) * kChunk;
             dst[f] = ld32(p, p + 64);
-            ds[f] = bsc[f][c];
         }
+#pragma unroll
+        for (int q = 0; q < NG; ++q) ds[q] = bsc[q][c];
     };
     auto load_a = [&](vec16 (&dst)[PASSES], float& ds, int c) __attribute__((always_inline)) {
 #pragma unroll
@@ -185,7 +198,7 @@ __global__ __launch_bounds__(kThreads, (BM <= 32 ? 2 : 1)) void gemm_fp8_kernel(
         for (int i = 0; i < PASSES; ++i) st16(&s_a[buf][a_st + i * ROWS_PER_PASS * kRowB], src[i]);
         if (tid < BM) s_sa[buf][tid] = ds;
     };
-    auto compute = [&](const i32x8v (&bv)[4], const float (&bs)[4], int buf) __attribute__((always_inline)) {
+    auto compute = [&](const i32x8v (&bv)[4], const float (&bs)[NG], int buf) __attribute__((always_inline)) {
         const unsigned char* src = s_a[buf];
         i32x8v af[2];
         f32x4 sa[2];
@@ -205,10 +218,12 @@ __global__ __launch_bounds__(kThreads, (BM <= 32 ? 2 : 1)) void gemm_fp8_kernel(
                 for (int f = 0; f < 4; ++f)
                     t[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[f], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
                                                                            0, 127, 0, 127);
+                // block dequantisation: acc += t * (a_scale[row] * w_scale)
+                f32x4 cs[NG];
 #pragma unroll
-                for (int f = 0; f < 4; ++f)
+                for (int q = 0; q < NG; ++q) cs[q] = sa[i & 1] * bs[q];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[i][f][v] += t[f][v] * (sa[i & 1][v] * bs[f]);
+                for (int f = 0; f < 4; ++f) acc[i][f] += t[f] * cs[NG == 2 ? f >> 1 : 0];
             }
         }
     };
@@ -341,7 +356,10 @@ GemmPlan plan_gemm_fp8(Epi epi, int64_t rows_upper, int n_groups, int64_t expect
     p.smajor = 0;
     p.big = 0;
     p.ksplit = 1;
-    p.bm = expected_rows_per_group <= 32 ? 32 : expected_rows_per_group <= 64 ? 64 : 128;
+    // 64-row tiles unless groups are large: the weight streams dominate and
+    // a 64-row tile keeps the dequantisation work per streamed byte low
+    // (measured: 64 faster than 128 at ~50 rows per active expert).
+    p.bm = expected_rows_per_group <= 32 ? 32 : expected_rows_per_group < 512 ? 64 : 128;
     const int cols = epi == Epi::SWIGLU ? 128 : 256;
     p.n_tiles = (N + cols - 1) / cols;
     const int64_t m_tiles = rows_upper / p.bm + n_groups;

@@ -110,6 +110,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 struct Profiler {
     bool on = false;
     int cap = 0, n = 0;
+    unsigned mask = ~0u;          // stages that record (bit s: stage s)
     std::vector<hipEvent_t> ev;   // 2 per record
     std::vector<int> stage;
 } g_prof;
@@ -118,7 +119,8 @@ struct StageTimer {
     int stage;
     hipStream_t s;
     bool active;
-    StageTimer(int st, hipStream_t str) : stage(st), s(str), active(g_prof.on && g_prof.n < g_prof.cap) {
+    StageTimer(int st, hipStream_t str)
+        : stage(st), s(str), active(g_prof.on && g_prof.n < g_prof.cap && ((g_prof.mask >> st) & 1u)) {
         if (active) {
             g_prof.stage[g_prof.n] = stage;
             hipEventRecord(g_prof.ev[2 * g_prof.n], s);
@@ -628,8 +630,10 @@ int moe_quantize_fp8(const moe_config* cfg, int64_t rows, const void* x, uint8_t
 
 int moe_profile_enable(int max_records) {
     if (max_records < 0) return MOE_ERR_INVALID_ARG;
+    const unsigned mask = g_prof.mask;          // the stage selection survives
     for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
     g_prof = Profiler{};
+    g_prof.mask = mask;
     if (max_records == 0) return MOE_OK;
     g_prof.ev.resize(2 * static_cast<size_t>(max_records));
     g_prof.stage.resize(max_records);
@@ -642,6 +646,11 @@ int moe_profile_enable(int max_records) {
 
 int moe_profile_reset(void) {
     g_prof.n = 0;
+    return MOE_OK;
+}
+
+int moe_profile_select(unsigned stage_mask) {
+    g_prof.mask = stage_mask;
     return MOE_OK;
 }
 
