@@ -35,7 +35,8 @@
  *  - When the routed experts get fewer than 128 rows each on average (decode
  *    shapes, bound by streaming weights), moe_expert_ffn and moe_forward run
  *    the shared expert on a second stream of the current device, forked from
- *    and joined back into `stream`, so it overlaps the routed path. That
+ *    and joined back into `stream`, so it overlaps the routed path (in
+ *    moe_forward from the router GEMM on, as it needs only x). That
  *    stream and two events are created on the first such call on a device and
  *    kept until the process ends; enqueueing on them is serialised by a lock,
  *    so calls from several host threads are safe.

@@ -593,19 +593,20 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
     int32_t* inv = at<int32_t>(ws, L.inv);
     void* rows = at<void>(ws, L.rows);
     void* shared_out = cfg->shared_inter > 0 ? at<void>(ws, L.shared_out) : nullptr;
-    // The small routing kernels run first, alone on the GPU; then the shared
-    // expert (which needs only x) runs on the side stream concurrently with
-    // the routed experts' grouped GEMMs.
+    // At decode shapes the shared expert (which needs only x) starts first,
+    // on the side stream, and runs beside the routing kernels and the routed
+    // experts' grouped GEMMs (measured on the EP8 decode share: 0.917 ->
+    // 0.892 ms per layer).
     std::lock_guard<std::mutex> lk(g_side_mu);
     SideStream* side = nullptr;
-    hipError_t e = do_router_gemm(cfg, T, x, w_router, router_bias, logits, ws, stream);
+    const bool overlap = overlap_shared(cfg, T);
+    hipError_t e = do_quant_x(cfg, T, x, ws, stream);
+    if (e == hipSuccess && overlap) e = fork_shared(cfg, T, x, weights, shared_out, ws, stream, &side);
+    if (e == hipSuccess) e = do_router_gemm(cfg, T, x, w_router, router_bias, logits, ws, stream);
     if (e == hipSuccess) e = do_route(cfg, T, logits, score_bias, ids, w, stream);
     if (e == hipSuccess)
         e = do_dispatch(cfg, T, ids, at<int32_t>(ws, L.raw), at<int32_t>(ws, L.counts), offsets, perm, inv, ws,
                         stream);
-    const bool overlap = overlap_shared(cfg, T);
-    if (e == hipSuccess) e = do_quant_x(cfg, T, x, ws, stream);
-    if (e == hipSuccess && overlap) e = fork_shared(cfg, T, x, weights, shared_out, ws, stream, &side);
     if (e == hipSuccess) e = do_routed_ffn(cfg, T, x, perm, offsets, weights, rows, ws, stream);
     if (side) {
         const hipError_t j = join_shared(side, stream);     // always rejoin the side stream
