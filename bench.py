@@ -266,6 +266,18 @@ def main():
     grouped = {"ms": gt * 1e3, "hbm_frac": gb / gt / 1e9 / PEAK_HBM_GBS,
                "mfma_frac": gf / gt / 1e12 / peak_mfma}
 
+    # expert load of this batch over all routed experts (device counts),
+    # and how an 8-GPU expert-parallel placement would balance it
+    load = torch.zeros(w["n_experts"], dtype=torch.int64, device="cuda")
+    moe.moe_expert_load(cfg, ids, load)
+    lc = load.cpu()
+    per = w["n_experts"] // 8
+    contig = lc.view(8, per).sum(1).double()
+    expert_load = {"hottest": int(lc.max()), "coldest": int(lc.min()), "mean": float(lc.double().mean()),
+                   "ep8_contiguous_imbalance": float(contig.max() / contig.mean()),
+                   "ep8_replanned_imbalance": moe.moe_eplb_plan(lc, 8, 0)[3],
+                   "ep8_replanned_8_redundant_imbalance": moe.moe_eplb_plan(lc, 8, 8)[3]}
+
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -277,6 +289,7 @@ def main():
         "grouped_gemm": grouped,
         "stage_ms": stage_ms,
         "rows": int(counts.sum()), "max_rows_per_expert": int(counts.max()),
+        "expert_load": expert_load,
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

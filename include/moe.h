@@ -219,6 +219,35 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
                 void* y, float* logits_out, int32_t* topk_ids_out,
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- Expert load statistics and placement ----------------------------------
+ * Infra guide "Data parallelism and expert parallelism", section 5: under
+ * expert parallelism every layer waits for the GPU that received the most
+ * tokens; the load each expert receives is recorded every step (5.3) and the
+ * experts are periodically re-placed, the hottest replicated (5.2, 5.3).
+ *
+ * moe_expert_load: adds to load[e] (device int64 [n_experts], 8-byte
+ * aligned; the caller zeroes it to start a window) the number of (token,
+ * slot) pairs among topk_ids (device int32 [T, top_k], as moe_route writes
+ * them) that chose expert e, for every global expert e (the router sees all
+ * experts whatever share this GPU holds). Exact integer counts.
+ *
+ * moe_eplb_plan (host only; all pointers are host memory): from per-expert
+ * loads [n_experts] (>= 0), places n_experts + n_redundant expert replicas on
+ * n_ranks GPUs, (n_experts + n_redundant) / n_ranks each (must divide
+ * evenly). Extra replicas go one at a time to the expert with the largest
+ * load per replica; then the replicas, heaviest first (load / replicas),
+ * go to the least-loaded GPU with a free slot. Ties: lowest expert id,
+ * lowest GPU index; equal replica loads keep (expert, replica) order.
+ * Writes replicas[n_experts], slot_expert[n_experts + n_redundant] (GPU g's
+ * slots are [g S, (g + 1) S), S = slots per GPU, in placement order),
+ * rank_load[n_ranks] (sum of load / replicas over the GPU's slots) and
+ * *imbalance = max rank load / mean rank load (1 = balanced; section 5.1).
+ * Returns MOE_ERR_INVALID_ARG on null pointers, non-positive counts, a
+ * negative load or slots that do not divide evenly. */
+int moe_expert_load(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int64_t* load, hipStream_t stream);
+int moe_eplb_plan(const int64_t* load, int n_experts, int n_ranks, int n_redundant, int32_t* replicas,
+                  int32_t* slot_expert, double* rank_load, double* imbalance);
+
 /* ---- Diagnostics: per-stage timing with HIP events ------------------------
  * Not part of the layer. moe_profile_enable(n) creates 2n HIP events and
  * starts recording: from then on every stage of every call records a start

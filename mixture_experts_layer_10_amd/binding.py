@@ -71,6 +71,9 @@ def lib():
             "moe_combine": (ctypes.c_int, [cfgp, i64, vp, i32p, fp, vp, vp, vp]),
             "moe_forward": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, wp, vp, fp, i32p, vp, ctypes.c_size_t, vp]),
             "moe_quantize_fp8": (ctypes.c_int, [cfgp, i64, vp, vp, fp, vp]),
+            "moe_expert_load": (ctypes.c_int, [cfgp, i64, vp, vp, vp]),
+            "moe_eplb_plan": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp,
+                                             ctypes.POINTER(ctypes.c_double)]),
             "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
             "moe_profile_reset": (ctypes.c_int, []),
             "moe_profile_select": (ctypes.c_int, [ctypes.c_uint]),
@@ -289,6 +292,30 @@ def moe_forward(cfg, x, w_router, router_bias, score_bias, weights, y, ws, logit
         _ptr(logits_out, torch.float32, (T, E), "logits_out", optional=True),
         _ptr(topk_ids_out, torch.int32, (T, cfg.top_k), "topk_ids_out", optional=True),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream)), "moe_forward")
+
+
+def moe_expert_load(cfg, topk_ids, load, stream=None):
+    """Adds the per-expert pair counts of topk_ids [T, k] (device int32) to load [E] (device int64)."""
+    T = topk_ids.shape[0]
+    _check(lib().moe_expert_load(
+        ctypes.byref(cfg), T, _ptr(topk_ids, torch.int32, (T, cfg.top_k), "topk_ids"),
+        _ptr(load, torch.int64, (cfg.n_experts,), "load"), _stream(stream)), "moe_expert_load")
+
+
+def moe_eplb_plan(load, n_ranks, n_redundant):
+    """Placement of E + R replicas on n_ranks GPUs from per-expert loads (a CPU
+    int64 tensor [E]). Returns (replicas [E], slot_expert [E + R], rank_load
+    [n_ranks], imbalance) as CPU tensors and a float."""
+    if load.device.type != "cpu" or load.dtype != torch.int64 or load.dim() != 1 or not load.is_contiguous():
+        raise ValueError("load must be a contiguous CPU int64 tensor [n_experts]")
+    E = load.numel()
+    replicas = torch.empty(E, dtype=torch.int32)
+    slots = torch.empty(E + max(n_redundant, 0), dtype=torch.int32)
+    rank_load = torch.empty(max(n_ranks, 1), dtype=torch.float64)
+    imb = ctypes.c_double(0.0)
+    _check(lib().moe_eplb_plan(load.data_ptr(), E, n_ranks, n_redundant, replicas.data_ptr(), slots.data_ptr(),
+                               rank_load.data_ptr(), ctypes.byref(imb)), "moe_eplb_plan")
+    return replicas, slots, rank_load, imb.value
 
 
 # ---------------------------------------------------------------------------

@@ -629,6 +629,33 @@ int moe_quantize_fp8(const moe_config* cfg, int64_t rows, const void* x, uint8_t
     return hip_status(launch_quant_fp8(x, q, scale, rows, cfg->hidden, stream));
 }
 
+int moe_expert_load(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int64_t* load, hipStream_t stream) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (T < 0) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!topk_ids || !load) return MOE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(load) % 8) return MOE_ERR_MISALIGNED;
+    return hip_status(launch_expert_load(topk_ids, T * cfg->top_k, cfg->n_experts, load, stream));
+}
+
+int moe_eplb_plan(const int64_t* load, int n_experts, int n_ranks, int n_redundant, int32_t* replicas,
+                  int32_t* slot_expert, double* rank_load, double* imbalance) {
+    if (!load || !replicas || !slot_expert || !rank_load || !imbalance) return MOE_ERR_INVALID_ARG;
+    if (n_experts <= 0 || n_ranks <= 0 || n_redundant < 0) return MOE_ERR_INVALID_ARG;
+    if ((static_cast<int64_t>(n_experts) + n_redundant) % n_ranks != 0) return MOE_ERR_INVALID_ARG;
+    for (int e = 0; e < n_experts; ++e)
+        if (load[e] < 0) return MOE_ERR_INVALID_ARG;
+    plan_placement(load, n_experts, n_ranks, n_redundant, replicas, slot_expert, rank_load);
+    double mx = rank_load[0], sum = 0.0;
+    for (int g = 0; g < n_ranks; ++g) {
+        mx = rank_load[g] > mx ? rank_load[g] : mx;
+        sum += rank_load[g];
+    }
+    *imbalance = sum > 0.0 ? mx / (sum / n_ranks) : 1.0;
+    return MOE_OK;
+}
+
 int moe_profile_enable(int max_records) {
     if (max_records < 0) return MOE_ERR_INVALID_ARG;
     const unsigned mask = g_prof.mask;          // the stage selection survives

@@ -110,6 +110,11 @@ hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* q, float* scale, int64_
 GemmPlan plan_gemm_fp8(Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N);
 hipError_t launch_gemm_fp8(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
 
+// --- expert load statistics and placement -----------------------------------
+hipError_t launch_expert_load(const int32_t* ids, int64_t n, int E, int64_t* load, hipStream_t s);
+void plan_placement(const int64_t* load, int E, int ranks, int redundant, int32_t* replicas, int32_t* slot_expert,
+                    double* rank_load);
+
 // --- combine (K7) ------------------------------------------------------------
 struct CombineArgs {
     const void* rows;         // [R, H]

@@ -49,8 +49,9 @@ def simulate_counts(seed=0, n_experts=256, top_k=8, tokens=4096, skew=0.4):
 
 
 def imbalance(loads):
-    """max / mean of per-GPU loads."""
-    return max(loads) / (sum(loads) / len(loads))
+    """max / mean of per-GPU loads (no load at all counts as balanced, 1)."""
+    total = sum(loads)
+    return max(loads) / (total / len(loads)) if total > 0 else 1.0
 
 
 def contiguous_loads(counts, ep):

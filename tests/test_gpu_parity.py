@@ -353,3 +353,31 @@ def test_forward_is_deterministic():
     torch.cuda.synchronize()
     for y in ys[1:]:
         assert torch.equal(y, ys[0])
+
+
+# ---------------------------------------------------------------------------
+# Expert load statistics (device) feeding the placement planner (host)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,T", [("ep8_decode_bf16", 256), ("fp8_skew", 300)])
+def test_expert_load_counts_and_plan(name, T):
+    """moe_expert_load counts every (token, slot) pair of the router's ids per
+    global expert, accumulating across calls; the planner then balances the
+    measured loads no worse than the contiguous placement."""
+    from oracle import eplb_oracle as P
+    w = workload(name, T=T)
+    say("expert load case", name, T)
+    run = Run(w, gen_device="cuda")
+    ids = torch.empty(T, w["top_k"], dtype=torch.int32, device="cuda")
+    run.forward(ids_out=ids)
+    load = torch.zeros(w["n_experts"], dtype=torch.int64, device="cuda")
+    moe.moe_expert_load(run.cfg, ids, load)
+    moe.moe_expert_load(run.cfg, ids, load)
+    torch.cuda.synchronize()
+    want = 2 * np.bincount(host(ids).reshape(-1), minlength=w["n_experts"])
+    assert np.array_equal(host(load), want)
+    counts = (host(load) // 2).tolist()
+    replicas, slots, rank_load, imb = moe.moe_eplb_plan(torch.tensor(counts, dtype=torch.int64), 8, 8)
+    r_o, s_o, l_o = P.balanced_placement(counts, 8, 8)
+    assert replicas.tolist() == r_o and rank_load.tolist() == l_o
+    assert imb <= P.imbalance(P.contiguous_loads(counts, 8)) + 1e-12
