@@ -79,17 +79,21 @@ def stored_traffic(stage, workload, dtype):
 
 def calibrate_copy(mib):
     """A plain copy kernel of known size: dst = src * 1 over `mib` MiB of
-    float32, five times; each launch reads and writes exactly mib MiB."""
+    float32, six times (the first untimed); each launch reads and writes
+    exactly mib MiB."""
     import torch
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)                     # warm-up launch (not counted below)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for _ in range(5):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
     print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4,
-                      "launches": 5}), flush=True)
+                      "launches": 6, "copy_gbs_read_plus_write": 2 * n * 4 / dt / 1e9}), flush=True)
 
 
 def stage_bytes_flops(w, counts, stage):
