@@ -24,6 +24,12 @@ What it computes, stage by stage, with the passage each stage follows:
             (an expert is three matrices gate, up, down) and Perplexity section
             "Quantization" (SiLU activation; FP8 weights with static scales per
             128x128 block, activations with dynamic scales per 1x128 vector).
+            FP4 expert weights: NVIDIA "Optimizing DeepSeek R1 throughput on
+            Blackwell", section on the FP4 checkpoint (the MoE layers' weights
+            are FP4). The pages fix no FP4 encoding; the reading here is the
+            OCP microscaling (MX) one: E2M1 elements, one E8M0 power-of-two
+            scale per 32 consecutive elements along the reduction dimension;
+            activations e4m3 with the same 32-element power-of-two scales.
   combine   glossary step 4 and infra guide section 3.1 step 4 (outputs come
             back and are summed weighted by the router scores); the shared
             expert sees every token and its output is added (Perplexity,
@@ -34,8 +40,9 @@ Routing decisions (an argmax over floating-point scores) are taken in float32
 with the recipe below, step for step, so that the GPU can match them bit for
 bit. Between stages the oracle rounds to the carrier type the layer uses: the
 intermediate activation h to the activation type (bf16 round-to-nearest-even,
-or e4m3 with 1x128 scales), and each routed expert's output row to bf16 when
-activations are bf16 or fp8 (the combine exchange carries BF16, infra guide
+e4m3 with 1x128 scales, or MX e4m3 with 32-element scales), and each routed
+expert's output row to bf16 when activations are bf16, fp8 or mxfp4 (the
+combine exchange carries BF16, infra guide
 section 3.2). The shared expert's output never leaves the token's GPU and is
 kept unrounded.
 
@@ -85,7 +92,7 @@ class Config:
     expert_begin: int = 0
     expert_end: int = -1
     capacity_factor: float = 0.0
-    act: str = "f32"          # "f32", "bf16" or "fp8"
+    act: str = "f32"          # "f32", "bf16", "fp8" or "mxfp4"
 
     def __post_init__(self):
         if self.expert_end < 0:
@@ -219,6 +226,85 @@ def dequant_block_weight(codes, scales):
     n, k = w.shape
     s = np.asarray(scales, dtype=np.float64)
     return (w.reshape(n // 128, 128, k // 128, 128) * s[:, None, :, None]).reshape(n, k)
+
+
+# ---------------------------------------------------------------------------
+# Microscaling (MX) formats: FP4 expert weights, e4m3 activations
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32
+E4M3_EMAX = 8          # largest e4m3 value 448 = 1.75 * 2**8
+E2M1_EMAX = 2          # largest e2m1 value 6 = 1.5 * 2**2
+
+
+def e2m1_decode(codes):
+    """E2M1 code (0..15) -> value (float64): sign bit 3, two exponent bits
+    with bias 1, one mantissa bit; exponent field 0 is subnormal (m * 0.5)."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    ex = (c >> 1) & 0x3
+    man = c & 0x1
+    val = np.where(ex == 0, man * 0.5, (1.0 + man / 2.0) * np.exp2(ex - 1.0))
+    return sign * val
+
+
+def e8m0_decode(codes):
+    """E8M0 scale code -> 2**(code - 127) (float64); code 255 is NaN."""
+    c = np.asarray(codes).astype(np.int64)
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+def unpack_fp4(packed):
+    """[..., K/2] bytes -> [..., K] E2M1 codes; element 2i is the low nibble of
+    byte i and element 2i+1 the high nibble."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def dequant_mx_weight(packed, scales):
+    """FP4 weight [N, K/2] bytes with E8M0 scales [N, K/32] -> float64 [N, K]:
+    element (n, k) is e2m1(code) * 2**(scale[n, k // 32] - 127)."""
+    v = e2m1_decode(unpack_fp4(packed))
+    n, k = v.shape
+    s = e8m0_decode(scales)
+    return (v.reshape(n, k // MX_BLOCK, MX_BLOCK) * s[:, :, None]).reshape(n, k)
+
+
+def mx_scale_exponent(amax, emax=E4M3_EMAX):
+    """Shared exponent of an MX block: floor(log2(amax)) - emax, kept within
+    the E8M0 range [-127, 127]; an all-zero block takes -127 (its codes are
+    zero whatever the scale)."""
+    a = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(a)                 # a = m * 2**e with 0.5 <= m < 1: floor(log2 a) = e - 1
+    x = np.where(a > 0, e - 1 - emax, -127)
+    return np.clip(x, -127, 127).astype(np.int64)
+
+
+def quantize_mx_rows(v):
+    """Per (row, 32-column block) MX e4m3 quantisation of float32 values.
+
+    X = mx_scale_exponent(max |v| over the block); each element becomes
+    e4m3_round(v * 2**-X) (the product is exact: a power of two), saturating
+    at +-448. Returns (q as float64 e4m3 values, scale codes uint8 X + 127,
+    [rows, cols/32]).
+    """
+    v = np.asarray(v, dtype=F32).astype(np.float64)
+    rows, cols = v.shape
+    blk = v.reshape(rows, cols // MX_BLOCK, MX_BLOCK)
+    x = mx_scale_exponent(np.max(np.abs(blk), axis=2))
+    q = e4m3_round(np.ldexp(blk, -x[:, :, None]))
+    return q.reshape(rows, cols), (x + 127).astype(np.uint8)
+
+
+def dequant_mx_rows(q, scale_codes):
+    """Values of MX-quantised rows: q [rows, cols] times 2**(code - 127) per
+    32-column block."""
+    rows, cols = q.shape
+    s = e8m0_decode(scale_codes)
+    return (np.asarray(q, dtype=np.float64).reshape(rows, cols // MX_BLOCK, MX_BLOCK) * s[:, :, None]).reshape(rows, cols)
 
 
 # ---------------------------------------------------------------------------
@@ -380,7 +466,9 @@ def swiglu_expert(cfg, x_rows, w13, w2, inter, w13_scale=None, w2_scale=None, ro
     x_rows: [n, H] input rows (their exact stored values). w13: [2I, H] with
     rows 0..I-1 the gate and I..2I-1 the up projection; w2: [H, I]. For fp8
     the weights are e4m3 codes with 128x128 block scales and the activations
-    are quantised per 1x128 block before each GEMM. Returns fp64 [n, H]; with
+    are quantised per 1x128 block before each GEMM; for mxfp4 the weights are
+    packed E2M1 codes with E8M0 scales per 32 along the input dimension and
+    the activations are MX e4m3 (32-element power-of-two scales). Returns fp64 [n, H]; with
     round_out (routed experts, whose outputs travel through the combine) the
     rows are rounded to their bf16 carrier when activations are bf16 or fp8.
     """
@@ -389,6 +477,10 @@ def swiglu_expert(cfg, x_rows, w13, w2, inter, w13_scale=None, w2_scale=None, ro
         W2 = dequant_block_weight(w2, w2_scale)
         qx, sx = quantize_fp8_rows(np.asarray(x_rows, dtype=F32))
         xa = (qx.reshape(len(qx), -1, 128) * sx.astype(np.float64)[:, :, None]).reshape(qx.shape)
+    elif cfg.act == "mxfp4":
+        W13 = dequant_mx_weight(w13, w13_scale)
+        W2 = dequant_mx_weight(w2, w2_scale)
+        xa = dequant_mx_rows(*quantize_mx_rows(np.asarray(x_rows, dtype=F32)))
     else:
         W13 = np.asarray(w13, dtype=np.float64)
         W2 = np.asarray(w2, dtype=np.float64)
@@ -399,10 +491,12 @@ def swiglu_expert(cfg, x_rows, w13, w2, inter, w13_scale=None, w2_scale=None, ro
     if cfg.act == "fp8":
         qh, sh = quantize_fp8_rows(h.astype(F32))
         ha = (qh.reshape(len(qh), -1, 128) * sh.astype(np.float64)[:, :, None]).reshape(qh.shape)
+    elif cfg.act == "mxfp4":
+        ha = dequant_mx_rows(*quantize_mx_rows(h.astype(F32)))
     else:
         ha = _round_act(h, cfg.act)
     o = ha @ W2.T
-    if round_out and cfg.act in ("bf16", "fp8"):
+    if round_out and cfg.act in ("bf16", "fp8", "mxfp4"):
         o = bf16_round(o)
     return o
 

@@ -12,7 +12,14 @@ Recipe (the pages name no dataset for this layer; these stand in for it):
     -1.1 * ln(rank_e) with rank_e = 1 + a seeded permutation of the experts;
   * bf16 tensors are the float32 draws rounded to nearest-even by torch;
   * fp8 weights are e4m3fn codes with one float32 scale per 128x128 block,
-    scale = block amax / 448, produced by torch's own float8 cast.
+    scale = block amax / 448, produced by torch's own float8 cast;
+  * mxfp4 weights are drawn directly as codes, not quantised from floats:
+    E2M1 codes two to a byte (element 2i in the low nibble), the sign fair,
+    the magnitude from a fixed table shaped like a normal sample that fills
+    the E2M1 range, and one E8M0 scale per 32 elements along the input
+    dimension, 2**floor(l) or 2**(floor(l) + 1) at random with
+    l = log2(std / rms(table)), so that the weights' RMS is about the same
+    1/sqrt(fan_in).
 
 Every tensor has its own torch.Generator, seeded from
 numpy.random.SeedSequence(seed, spawn_key=(tensor_id, global_expert)), so any
@@ -68,8 +75,34 @@ def zipf_router_bias(n_experts, s=1.1, seed=0):
     return torch.tensor(-s * np.log(rank.astype(np.float64)), dtype=torch.float32)
 
 
+# Magnitude distribution of the synthetic E2M1 codes 0..7 (values 0, 0.5, 1,
+# 1.5, 2, 3, 4, 6): about what a normal sample scaled so that its largest
+# value reaches 4..8 looks like on that grid.
+FP4_MAG_PROBS = (0.07, 0.14, 0.14, 0.13, 0.18, 0.15, 0.13, 0.06)
+FP4_MAG_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+MX_BLOCK = 32
+
+
+def _fp4_codes(shape, std, device, seed, tensor, expert):
+    """Random packed E2M1 codes [N, K/2] and E8M0 scales [N, K/32] (uint8)."""
+    n, k = shape
+    g = _gen(device, seed, tensor, expert)
+    cdf = torch.tensor(np.cumsum(FP4_MAG_PROBS)[:-1], dtype=torch.float32, device=device)
+    mag = torch.bucketize(torch.rand((n, k), generator=g, device=device), cdf, right=True)
+    sign = (torch.rand((n, k), generator=g, device=device) < 0.5).to(torch.int64) << 3
+    codes = (mag | sign).to(torch.uint8)
+    packed = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    rms = math.sqrt(sum(p * v * v for p, v in zip(FP4_MAG_PROBS, FP4_MAG_VALUES)))
+    lg = math.log2(std / rms)
+    base = math.floor(lg)
+    up = (torch.rand((n, k // MX_BLOCK), generator=g, device=device) < (lg - base)).to(torch.int64)
+    scales = (127 + base + up).to(torch.uint8)
+    return packed.contiguous(), scales.contiguous()
+
+
 def _weight_dtype(w):
-    return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.bfloat16}[w["dtype"]]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.bfloat16,
+            "mxfp4": torch.bfloat16}[w["dtype"]]
 
 
 def make_inputs(w, device="cpu", seed=0):
@@ -77,7 +110,8 @@ def make_inputs(w, device="cpu", seed=0):
 
     Returns a dict with x, w_router, router_bias (or None), score_bias (or None),
     w13, w2, shared_w13, shared_w2 (None when there is no shared expert) and,
-    for fp8, w13_scale, w2_scale, shared_w13_scale, shared_w2_scale.
+    for fp8 and mxfp4, w13_scale, w2_scale, shared_w13_scale, shared_w2_scale.
+    mxfp4 weights are uint8: packed codes [.., N, K/2], scales [.., N, K/32].
     """
     T, H, E, I = w["T"], w["hidden"], w["n_experts"], w["inter"]
     Is = w["shared_inter"]
@@ -85,6 +119,7 @@ def make_inputs(w, device="cpu", seed=0):
     b0 = w["expert_begin"]
     act_dtype = _weight_dtype(w)
     fp8 = w["dtype"] == "fp8"
+    fp4 = w["dtype"] == "mxfp4"
     out = {}
 
     out["x"] = _normal((T, H), 1.0, device, seed, "x").to(act_dtype)
@@ -109,6 +144,12 @@ def make_inputs(w, device="cpu", seed=0):
         raise ValueError(rb)
 
     def expert_stack(name, n_rows, n_cols, experts, std):
+        if fp4:
+            codes = torch.empty((len(experts), n_rows, n_cols // 2), dtype=torch.uint8, device=device)
+            scales = torch.empty((len(experts), n_rows, n_cols // MX_BLOCK), dtype=torch.uint8, device=device)
+            for i, e in enumerate(experts):
+                codes[i], scales[i] = _fp4_codes((n_rows, n_cols), std, device, seed, name, e)
+            return codes, scales
         if fp8:
             codes = torch.empty((len(experts), n_rows, n_cols), dtype=torch.float8_e4m3fn, device=device)
             scales = torch.empty((len(experts), n_rows // BLOCK, n_cols // BLOCK), dtype=torch.float32, device=device)
@@ -133,8 +174,8 @@ def make_inputs(w, device="cpu", seed=0):
         s13, s13s = expert_stack("shared_w13", 2 * Is, H, [0], 1.0 / math.sqrt(H))
         s2, s2s = expert_stack("shared_w2", H, Is, [0], 1.0 / math.sqrt(Is))
         out["shared_w13"], out["shared_w2"] = s13[0], s2[0]
-        out["shared_w13_scale"] = s13s[0] if fp8 else None
-        out["shared_w2_scale"] = s2s[0] if fp8 else None
+        out["shared_w13_scale"] = s13s[0] if (fp8 or fp4) else None
+        out["shared_w2_scale"] = s2s[0] if (fp8 or fp4) else None
     else:
         out["shared_w13"] = out["shared_w2"] = None
         out["shared_w13_scale"] = out["shared_w2_scale"] = None

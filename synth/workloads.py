@@ -20,7 +20,8 @@ Keys:
   routed_scale gamma, the routed scaling factor
   inter        I, expert intermediate size
   shared_inter I_s, shared-expert intermediate size (0 = no shared expert)
-  dtype        "f32", "bf16" or "fp8" (weights; activations follow)
+  dtype        "f32", "bf16", "fp8" or "mxfp4" (weights; activations follow:
+               bf16 in, e4m3 at the expert GEMMs for fp8 and mxfp4)
   capacity_factor  <= 0 means no capacity limit
   score_bias   "none", "zero", "normal0.01" or "normal0.1" (selection-only bias)
   router_bias  "none" or "zipf1.1" (linear bias of the router GEMM)
@@ -53,6 +54,11 @@ WORKLOADS = {
     "fp8_skew": dict(_BASE_DSV3, T=8192, expert_begin=0, expert_end=256,
                      dtype="fp8", score_bias="zero", capacity_factor=1.25,
                      router_bias="zipf1.1"),
+    # Whole 256-expert layer, decode batch, with FP4 (MX) expert weights: the
+    # weight-bandwidth-bound shape where FP4 halves the bytes again (NVIDIA,
+    # "Optimizing DeepSeek R1 throughput on Blackwell", FP4 checkpoint).
+    "full_decode_mxfp4": dict(_BASE_DSV3, T=512, expert_begin=0, expert_end=256,
+                              dtype="mxfp4", score_bias="normal0.01"),
 }
 
 ORDER = ["toy_fp32", "ep8_decode_bf16", "full_decode_bf16", "full_prefill_bf16", "fp8_skew"]
