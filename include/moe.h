@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 enum moe_status {
@@ -78,11 +78,19 @@ enum moe_score_fn {
  *         (static); hidden states come in bf16 and are quantised to e4m3 with
  *         one fp32 scale per 1x128 block before the gate/up GEMM, h likewise
  *         before the down GEMM (dynamic); expert output rows bf16; the router
- *         weight stays bf16. (Perplexity, section "Quantization".) */
+ *         weight stays bf16. (Perplexity, section "Quantization".)
+ *  MXFP4: expert weights FP4 (E2M1) with one E8M0 power-of-two scale per 32
+ *         consecutive elements along the input dimension (OCP microscaling);
+ *         hidden states come in bf16 and are quantised to e4m3 with one E8M0
+ *         scale per 1x32 block before the gate/up GEMM, h likewise before the
+ *         down GEMM; expert output rows bf16; the router weight stays bf16.
+ *         (NVIDIA "Optimizing DeepSeek R1 throughput on Blackwell": the MoE
+ *         layers' weights in FP4.) Needs H, I and I_s multiples of 256. */
 enum moe_dtype {
     MOE_DTYPE_F32 = 0,
     MOE_DTYPE_BF16 = 1,
-    MOE_DTYPE_FP8 = 2
+    MOE_DTYPE_FP8 = 2,
+    MOE_DTYPE_MXFP4 = 3
 };
 
 typedef struct moe_config {
@@ -109,17 +117,21 @@ typedef struct moe_config {
  *  w13       [E_l, 2I, H]: rows 0..I-1 gate, I..2I-1 up projection
  *  w2        [E_l, H, I]:  down projection
  *  shared_*  the same for the shared expert with I_s ([2 I_s, H], [H, I_s])
- *  *_scale   FP8 only: fp32 [E_l, 2I/128, H/128], [E_l, H/128, I/128] and
- *            [2 I_s/128, H/128], [H/128, I_s/128]; NULL otherwise. */
+ *  *_scale   FP8: fp32 [E_l, 2I/128, H/128], [E_l, H/128, I/128] and
+ *            [2 I_s/128, H/128], [H/128, I_s/128];
+ *            MXFP4: E8M0 bytes [E_l, 2I, H/32], [E_l, H, I/32] and
+ *            [2 I_s, H/32], [H, I_s/32] (8-byte aligned); NULL otherwise.
+ * MXFP4 weight rows are packed two E2M1 codes per byte, element 2i in the low
+ * nibble: w13 [E_l, 2I, H/2] bytes, w2 [E_l, H, I/2] bytes. */
 typedef struct moe_weights {
     const void* w13;
     const void* w2;
-    const float* w13_scale;
-    const float* w2_scale;
+    const void* w13_scale;
+    const void* w2_scale;
     const void* shared_w13;
     const void* shared_w2;
-    const float* shared_w13_scale;
-    const float* shared_w2_scale;
+    const void* shared_w13_scale;
+    const void* shared_w2_scale;
 } moe_weights;
 
 int moe_abi_version(void);
@@ -136,7 +148,7 @@ int moe_validate_config(const moe_config* cfg);
 int moe_workspace_bytes(const moe_config* cfg, int64_t max_tokens, size_t* bytes);
 
 /* Router GEMM: logits[T, E] (fp32) = x[T, H] . w_router[E, H]^T + router_bias.
- * x and w_router are fp32 (F32) or bf16 (BF16, FP8): inputs of the activation
+ * x and w_router are fp32 (F32) or bf16 (BF16, FP8, MXFP4): inputs of the activation
  * type in, fp32 out, no separate cast (NVIDIA, "MoE layer optimisations >
  * mixed I/O RouterGEMM"). router_bias [E] fp32 may be NULL. All device; the
  * workspace holds split-K partial sums. */
@@ -182,7 +194,7 @@ int moe_dispatch(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int3
  * with t = perm[r] / k; and for every token, the shared expert's output in
  * shared_out[t] (if shared_inter > 0). Group sizes are read from `offsets`
  * on the device, so no host synchronisation is needed.
- *  x          [T, H] device, activation type (bf16 for FP8)
+ *  x          [T, H] device, activation type (bf16 for FP8 and MXFP4)
  *  perm, offsets  from moe_dispatch
  *  out_rows   [T*k, H] device out (fp32 for F32, bf16 otherwise: the rows are
  *             what the combine exchange carries); rows >= R untouched
@@ -209,8 +221,19 @@ int moe_combine(const moe_config* cfg, int64_t T, const void* out_rows, const in
 int moe_quantize_fp8(const moe_config* cfg, int64_t rows, const void* x, uint8_t* q, float* scale,
                      hipStream_t stream);
 
+/* MX activation quantisation for MXFP4 layers (OCP microscaling, the
+ * activation side of FP4 expert weights): for each row and each block of 32
+ * columns, X = floor(log2(max |x|)) - 8 clamped to [-127, 127] (-127 for an
+ * all-zero block); codes = e4m3(x * 2**-X) (OCP E4M3FN, round to nearest
+ * even, saturating at +-448; the product is exact); scale code = X + 127.
+ *  x [rows, H] bf16 device; q [rows, H] uint8 codes out; scale [rows, H/32]
+ *  uint8 E8M0 out. cfg->dtype must be MOE_DTYPE_MXFP4; moe_expert_ffn and
+ *  moe_forward apply the same quantisation to x internally. */
+int moe_quantize_mx(const moe_config* cfg, int64_t rows, const void* x, uint8_t* q, uint8_t* scale,
+                    hipStream_t stream);
+
 /* The whole layer: router GEMM, route, dispatch, experts, combine.
- *  x [T, H], w_router [E, H] (activation type; bf16 for FP8), router_bias [E]
+ *  x [T, H], w_router [E, H] (activation type; bf16 for FP8 and MXFP4), router_bias [E]
  *  and score_bias [E] fp32 or NULL, weights as above; y [T, H] out.
  *  logits_out [T, E] fp32 and topk_ids_out [T, k] int32, if not NULL, receive
  *  the router logits and expert ids. */
@@ -268,7 +291,7 @@ enum moe_stage {
     MOE_STAGE_SHARED_GATE_UP = 5,
     MOE_STAGE_SHARED_DOWN = 6,
     MOE_STAGE_COMBINE = 7,
-    MOE_STAGE_QUANT = 8,            /* FP8: activation quantisation of x */
+    MOE_STAGE_QUANT = 8,            /* FP8, MXFP4: activation quantisation of x */
     MOE_STAGE_COUNT = 9
 };
 int moe_profile_enable(int max_records);

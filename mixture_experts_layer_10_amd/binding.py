@@ -14,11 +14,11 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_MISALIGNED, ERR_HIP, ERR_ABI_MISMATCH = \
     0, -1, -2, -3, -4, -5, -6
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
-DTYPE_F32, DTYPE_BF16, DTYPE_FP8 = 0, 1, 2
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8, DTYPE_MXFP4 = 0, 1, 2, 3
 
 
 class MoEError(RuntimeError):
@@ -71,6 +71,7 @@ def lib():
             "moe_combine": (ctypes.c_int, [cfgp, i64, vp, i32p, fp, vp, vp, vp]),
             "moe_forward": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, wp, vp, fp, i32p, vp, ctypes.c_size_t, vp]),
             "moe_quantize_fp8": (ctypes.c_int, [cfgp, i64, vp, vp, fp, vp]),
+            "moe_quantize_mx": (ctypes.c_int, [cfgp, i64, vp, vp, vp, vp]),
             "moe_expert_load": (ctypes.c_int, [cfgp, i64, vp, vp, vp]),
             "moe_eplb_plan": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp,
                                              ctypes.POINTER(ctypes.c_double)]),
@@ -103,7 +104,7 @@ def _check(status, where):
 # Configuration
 # ---------------------------------------------------------------------------
 
-_DT = {"f32": DTYPE_F32, "bf16": DTYPE_BF16, "fp8": DTYPE_FP8}
+_DT = {"f32": DTYPE_F32, "bf16": DTYPE_BF16, "fp8": DTYPE_FP8, "mxfp4": DTYPE_MXFP4}
 
 
 def make_config(hidden, n_experts, top_k, inter, *, expert_begin=0, expert_end=None, n_group=1,
@@ -186,7 +187,11 @@ def _stream(stream):
 
 
 def _weight_dtype(cfg):
-    return torch.float8_e4m3fn if cfg.dtype == DTYPE_FP8 else _act_dtype(cfg)
+    if cfg.dtype == DTYPE_FP8:
+        return torch.float8_e4m3fn
+    if cfg.dtype == DTYPE_MXFP4:
+        return torch.uint8                    # two E2M1 codes per byte
+    return _act_dtype(cfg)
 
 
 def make_weights(cfg, w13, w2, shared_w13=None, shared_w2=None, w13_scale=None, w2_scale=None,
@@ -195,11 +200,19 @@ def make_weights(cfg, w13, w2, shared_w13=None, shared_w2=None, w13_scale=None, 
     El, H, I, Is = cfg.n_local, cfg.hidden, cfg.inter, cfg.shared_inter
     wd = _weight_dtype(cfg)
     W = Weights()
-    W.w13 = _ptr(w13, wd, (El, 2 * I, H), "w13")
-    W.w2 = _ptr(w2, wd, (El, H, I), "w2")
+    pk = 2 if cfg.dtype == DTYPE_MXFP4 else 1        # elements per stored byte/element along K
+    W.w13 = _ptr(w13, wd, (El, 2 * I, H // pk), "w13")
+    W.w2 = _ptr(w2, wd, (El, H, I // pk), "w2")
     if Is > 0:
-        W.shared_w13 = _ptr(shared_w13, wd, (2 * Is, H), "shared_w13")
-        W.shared_w2 = _ptr(shared_w2, wd, (H, Is), "shared_w2")
+        W.shared_w13 = _ptr(shared_w13, wd, (2 * Is, H // pk), "shared_w13")
+        W.shared_w2 = _ptr(shared_w2, wd, (H, Is // pk), "shared_w2")
+    if cfg.dtype == DTYPE_MXFP4:
+        u8 = torch.uint8
+        W.w13_scale = _ptr(w13_scale, u8, (El, 2 * I, H // 32), "w13_scale")
+        W.w2_scale = _ptr(w2_scale, u8, (El, H, I // 32), "w2_scale")
+        if Is > 0:
+            W.shared_w13_scale = _ptr(shared_w13_scale, u8, (2 * Is, H // 32), "shared_w13_scale")
+            W.shared_w2_scale = _ptr(shared_w2_scale, u8, (H, Is // 32), "shared_w2_scale")
     if cfg.dtype == DTYPE_FP8:
         f32 = torch.float32
         W.w13_scale = _ptr(w13_scale, f32, (El, 2 * I // 128, H // 128), "w13_scale")
@@ -268,6 +281,15 @@ def moe_combine(cfg, out_rows, inv, topk_w, shared_out, y, stream=None):
         _ptr(topk_w, torch.float32, (T, k), "topk_w"),
         _ptr(shared_out, torch.float32, (T, H), "shared_out", optional=True),
         _ptr(y, _out_dtype(cfg), (T, H), "y"), _stream(stream)), "moe_combine")
+
+
+def moe_quantize_mx(cfg, x, q, scale, stream=None):
+    """x [rows, H] bf16 -> e4m3 codes q [rows, H] (uint8) and E8M0 scale codes [rows, H/32] (uint8)."""
+    rows, H = x.shape[0], cfg.hidden
+    _check(lib().moe_quantize_mx(
+        ctypes.byref(cfg), rows, _ptr(x, torch.bfloat16, (rows, H), "x"),
+        _ptr(q, torch.uint8, (rows, H), "q"), _ptr(scale, torch.uint8, (rows, H // 32), "scale"),
+        _stream(stream)), "moe_quantize_mx")
 
 
 def moe_quantize_fp8(cfg, x, q, scale, stream=None):

@@ -126,7 +126,8 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
     const int nb_rows = (EPI == Epi::SWIGLU ? 2 * a.inter : a.N) / 128;      // scale rows per expert
     const unsigned char* Bg = shared ? static_cast<const unsigned char*>(a.B_shared)
                                      : static_cast<const unsigned char*>(a.B) + static_cast<int64_t>(g) * a.b_stride;
-    const float* Sg = shared ? a.B_scale_shared : a.B_scale + static_cast<int64_t>(g) * nb_rows * kblocks;
+    const float* Sg = shared ? static_cast<const float*>(a.B_scale_shared)
+                             : static_cast<const float*>(a.B_scale) + static_cast<int64_t>(g) * nb_rows * kblocks;
     uint32_t boff[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
     // ---- activations: gathered e4m3 rows and their per-block scales --------
     const int aj = tid % ROWG, ar = tid / ROWG;
     const unsigned char* Abase = static_cast<const unsigned char*>(shared ? a.A_shared : a.A) + aj * 16;
-    const float* Ascale = shared ? a.A_scale_shared : a.A_scale;
+    const float* Ascale = static_cast<const float*>(shared ? a.A_scale_shared : a.A_scale);
     auto src_row = [&](int r) -> uint32_t {
         r = r < rows ? r : rows - 1;
         if (shared) return m0 + r;
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
             }
         __syncthreads();
         uint8_t* Cq = static_cast<uint8_t*>(shared ? a.C_shared : a.C);
-        float* Cs = shared ? a.C_scale_shared : a.C_scale;
+        float* Cs = static_cast<float*>(shared ? a.C_scale_shared : a.C_scale);
         const int nsb = a.N / 128;
 #pragma unroll
         for (int i = 0; i < NRF; ++i) {

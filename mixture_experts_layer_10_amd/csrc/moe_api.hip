@@ -36,13 +36,17 @@ int validate(const moe_config* c) {
     if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
     if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
     if (!isfinite(c->routed_scale) || !isfinite(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
-    if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16 && c->dtype != MOE_DTYPE_FP8)
+    if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16 && c->dtype != MOE_DTYPE_FP8 &&
+        c->dtype != MOE_DTYPE_MXFP4)
         return MOE_ERR_INVALID_ARG;
     if (c->out_dtype != MOE_DTYPE_F32 && c->out_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
     // Valid, but outside what the kernels are built for.
     if (c->top_k > 16 || c->n_experts > 512 || c->n_group > 64) return MOE_ERR_UNSUPPORTED;
     if (c->expert_end - c->expert_begin > 1024) return MOE_ERR_UNSUPPORTED;
     if (c->hidden % 128 != 0 || c->inter % 128 != 0 || c->shared_inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    // The FP4 GEMM reduces K in chunks of 256 (one 128-byte line per weight row).
+    if (c->dtype == MOE_DTYPE_MXFP4 && (c->hidden % 256 != 0 || c->inter % 256 != 0 || c->shared_inter % 256 != 0))
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -50,11 +54,21 @@ int act_bytes(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 4 : c->d
 int row_bytes(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 4 : 2; }
 Elem gemm_elem(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? Elem::F32 : Elem::BF16; }
 
+// Expert GEMMs on e4m3 activations: FP8 block-scaled or MX (FP4 weights).
+bool quantised(const moe_config* c) { return c->dtype == MOE_DTYPE_FP8 || c->dtype == MOE_DTYPE_MXFP4; }
+GemmPlan plan_quantised(const moe_config* c, Epi epi, int64_t rows_upper, int n_groups, int64_t per_group, int N) {
+    return c->dtype == MOE_DTYPE_MXFP4 ? plan_gemm_mx(epi, rows_upper, n_groups, per_group, N)
+                                      : plan_gemm_fp8(epi, rows_upper, n_groups, per_group, N);
+}
+hipError_t launch_quantised(const moe_config* c, Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    return c->dtype == MOE_DTYPE_MXFP4 ? launch_gemm_mx(epi, a, p, s) : launch_gemm_fp8(epi, a, p, s);
+}
+
 // Workspace layout for up to T tokens; every region 256-byte aligned.
 struct Layout {
     size_t logits, ids, w, raw, counts, offsets, perm, inv, chunk_hist, chunk_base, sched, partial;
     size_t h, h_shared, rows, shared_out;
-    size_t xq, xs, hs, hs_shared;       // FP8: quantised x and the scales of x and h
+    size_t xq, xs, hs, hs_shared;       // FP8, MXFP4: quantised x and the scales of x and h
     size_t total;
 };
 
@@ -88,11 +102,15 @@ Layout layout(const moe_config* c, int64_t T) {
     L.h_shared = take(static_cast<size_t>(act_bytes(c)) * T * c->shared_inter);
     L.rows = take(static_cast<size_t>(row_bytes(c)) * P * c->hidden);
     L.shared_out = take(sizeof(float) * T * c->hidden);
-    const bool fp8 = c->dtype == MOE_DTYPE_FP8;
-    L.xq = take(fp8 ? static_cast<size_t>(T) * c->hidden : 0);
-    L.xs = take(fp8 ? sizeof(float) * T * (c->hidden / 128) : 0);
-    L.hs = take(fp8 ? sizeof(float) * P * (c->inter / 128) : 0);
-    L.hs_shared = take(fp8 ? sizeof(float) * T * (c->shared_inter / 128) : 0);
+    // scale bytes per activation element: FP8 one float per 128, MXFP4 one byte per 32
+    const bool fp8 = c->dtype == MOE_DTYPE_FP8, mx = c->dtype == MOE_DTYPE_MXFP4;
+    auto sbytes = [&](int64_t rows, int64_t cols) -> size_t {
+        return fp8 ? sizeof(float) * rows * (cols / 128) : mx ? static_cast<size_t>(rows) * (cols / 32) : 0;
+    };
+    L.xq = take(fp8 || mx ? static_cast<size_t>(T) * c->hidden : 0);
+    L.xs = take(sbytes(T, c->hidden));
+    L.hs = take(sbytes(P, c->inter));
+    L.hs_shared = take(sbytes(T, c->shared_inter));
     L.total = off;
     return L;
 }
@@ -240,27 +258,30 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
     g1.C = g1.C_shared = at<void>(ws, L.h);
     g1.ldc = static_cast<int>(I);
     const int64_t per_expert = (P + c->n_experts - 1) / c->n_experts;
-    if (c->dtype == MOE_DTYPE_FP8) {
-        // e4m3 operands: x quantised by the caller (moe_quantize_fp8 layout in
-        // the workspace), h requantised by the gate/up epilogue.
+    if (quantised(c)) {
+        // e4m3 operands: x quantised into the workspace by do_quant_x, h
+        // requantised by the gate/up epilogue; FP8 (1x128 fp32 scales, 128x128
+        // weight blocks) or MX (E8M0 scales per 32, FP4 weights).
+        const bool mx = c->dtype == MOE_DTYPE_MXFP4;
         g1.A = g1.A_shared = at<void>(ws, L.xq);
-        g1.A_scale = g1.A_scale_shared = at<float>(ws, L.xs);
+        g1.A_scale = g1.A_scale_shared = at<void>(ws, L.xs);
         g1.B_scale = g1.B_scale_shared = wt->w13_scale;
-        g1.C_scale = g1.C_scale_shared = at<float>(ws, L.hs);
-        const GemmPlan p1 = plan_gemm_fp8(Epi::SWIGLU, P, El, per_expert, static_cast<int>(I));
+        g1.C_scale = g1.C_scale_shared = at<void>(ws, L.hs);
+        g1.b_stride = mx ? I * H : 2 * I * H;                  // bytes between experts
+        const GemmPlan p1 = plan_quantised(c, Epi::SWIGLU, P, El, per_expert, static_cast<int>(I));
         if ((e = launch_schedule(g1, p1.bm, sched, s)) != hipSuccess) return e;
         {
             StageTimer tm(MOE_STAGE_GATE_UP, s);
-            if ((e = launch_gemm_fp8(Epi::SWIGLU, g1, p1, s)) != hipSuccess) return e;
+            if ((e = launch_quantised(c, Epi::SWIGLU, g1, p1, s)) != hipSuccess) return e;
         }
         GemmArgs g2 = g1;
         g2.A = g2.A_shared = at<void>(ws, L.h);
-        g2.A_scale = g2.A_scale_shared = at<float>(ws, L.hs);
+        g2.A_scale = g2.A_scale_shared = at<void>(ws, L.hs);
         g2.perm = nullptr;
         g2.gather = 0;
         g2.B = g2.B_shared = wt->w2;
         g2.B_scale = g2.B_scale_shared = wt->w2_scale;
-        g2.b_stride = H * I;
+        g2.b_stride = mx ? H * I / 2 : H * I;
         g2.K = static_cast<int>(I);
         g2.N = static_cast<int>(H);
         g2.inter = 0;
@@ -268,9 +289,11 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
         g2.C_scale = g2.C_scale_shared = nullptr;
         g2.ldc = static_cast<int>(H);
         g2.out_f32 = 0;
-        GemmPlan p2 = plan_gemm_fp8(Epi::PLAIN, P, El, per_expert, static_cast<int>(H));
+        // the down GEMM reuses the gate/up schedule's m-tiles: same row tile
+        const GemmPlan p2 = plan_quantised(c, Epi::PLAIN, P, El, per_expert, static_cast<int>(H));
+        if (p2.bm != p1.bm) return hipErrorInvalidValue;
         StageTimer tm(MOE_STAGE_DOWN, s);
-        return launch_gemm_fp8(Epi::PLAIN, g2, p2, s);
+        return launch_quantised(c, Epi::PLAIN, g2, p2, s);
     }
     const GemmPlan p1 = plan_gemm(el, Epi::SWIGLU, P, El, per_expert, static_cast<int>(I));
     if ((e = launch_schedule(g1, p1.bm, sched, s)) != hipSuccess) return e;
@@ -326,19 +349,19 @@ hipError_t do_shared_ffn(const moe_config* c, int64_t T, const void* x, const mo
     s1.inter = static_cast<int>(Is);
     s1.C = s1.C_shared = at<void>(ws, L.h_shared);
     s1.ldc = static_cast<int>(Is);
-    if (c->dtype == MOE_DTYPE_FP8) {
+    if (quantised(c)) {
         s1.A = s1.A_shared = at<void>(ws, L.xq);
-        s1.A_scale = s1.A_scale_shared = at<float>(ws, L.xs);
+        s1.A_scale = s1.A_scale_shared = at<void>(ws, L.xs);
         s1.B_scale = s1.B_scale_shared = wt->shared_w13_scale;
-        s1.C_scale = s1.C_scale_shared = at<float>(ws, L.hs_shared);
-        const GemmPlan q1 = plan_gemm_fp8(Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
+        s1.C_scale = s1.C_scale_shared = at<void>(ws, L.hs_shared);
+        const GemmPlan q1 = plan_quantised(c, Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
         {
             StageTimer tm(MOE_STAGE_SHARED_GATE_UP, s);
-            if ((e = launch_gemm_fp8(Epi::SWIGLU, s1, q1, s)) != hipSuccess) return e;
+            if ((e = launch_quantised(c, Epi::SWIGLU, s1, q1, s)) != hipSuccess) return e;
         }
         GemmArgs s2 = s1;
         s2.A = s2.A_shared = at<void>(ws, L.h_shared);
-        s2.A_scale = s2.A_scale_shared = at<float>(ws, L.hs_shared);
+        s2.A_scale = s2.A_scale_shared = at<void>(ws, L.hs_shared);
         s2.B = s2.B_shared = wt->shared_w2;
         s2.B_scale = s2.B_scale_shared = wt->shared_w2_scale;
         s2.K = static_cast<int>(Is);
@@ -348,9 +371,9 @@ hipError_t do_shared_ffn(const moe_config* c, int64_t T, const void* x, const mo
         s2.C_scale = s2.C_scale_shared = nullptr;
         s2.ldc = static_cast<int>(H);
         s2.out_f32 = 1;
-        const GemmPlan q2 = plan_gemm_fp8(Epi::PLAIN, T, 1, T, static_cast<int>(H));
+        const GemmPlan q2 = plan_quantised(c, Epi::PLAIN, T, 1, T, static_cast<int>(H));
         StageTimer tm(MOE_STAGE_SHARED_DOWN, s);
-        return launch_gemm_fp8(Epi::PLAIN, s2, q2, s);
+        return launch_quantised(c, Epi::PLAIN, s2, q2, s);
     }
     const GemmPlan q1 = plan_gemm(el, Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
     {
@@ -420,12 +443,14 @@ bool overlap_shared(const moe_config* c, int64_t T) {
     return c->shared_inter > 0 && T * c->top_k < 128LL * c->n_experts;
 }
 
-// FP8: x -> e4m3 codes + per-(row, 128 columns) scales in the workspace,
-// read by both the routed and the shared gate/up GEMMs.
+// FP8 / MXFP4: x -> e4m3 codes + per-(row, 128 or 32 columns) scales in the
+// workspace, read by both the routed and the shared gate/up GEMMs.
 hipError_t do_quant_x(const moe_config* c, int64_t T, const void* x, void* ws, hipStream_t s) {
-    if (c->dtype != MOE_DTYPE_FP8) return hipSuccess;
+    if (!quantised(c)) return hipSuccess;
     const Layout L = layout(c, T);
     StageTimer tm(MOE_STAGE_QUANT, s);
+    if (c->dtype == MOE_DTYPE_MXFP4)
+        return launch_quant_mx(x, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), T, c->hidden, s);
     return launch_quant_fp8(x, at<uint8_t>(ws, L.xq), at<float>(ws, L.xs), T, c->hidden, s);
 }
 
@@ -470,9 +495,13 @@ bool weights_ok(const moe_config* c, const moe_weights* w) {
     if (c->shared_inter > 0 && (!w->shared_w13 || !w->shared_w2 || !aligned16(w->shared_w13) ||
                                 !aligned16(w->shared_w2)))
         return false;
-    if (c->dtype == MOE_DTYPE_FP8) {
+    if (quantised(c)) {
         if (!w->w13_scale || !w->w2_scale) return false;
         if (c->shared_inter > 0 && (!w->shared_w13_scale || !w->shared_w2_scale)) return false;
+        // MX scale rows are read 8 bytes at a time
+        auto al8 = [](const void* p) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % 8 == 0; };
+        if (!al8(w->w13_scale) || !al8(w->w2_scale) || !al8(w->shared_w13_scale) || !al8(w->shared_w2_scale))
+            return false;
     }
     return true;
 }
@@ -627,6 +656,18 @@ int moe_quantize_fp8(const moe_config* cfg, int64_t rows, const void* x, uint8_t
     if (!x || !q || !scale) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(q) || !aligned16(scale)) return MOE_ERR_MISALIGNED;
     return hip_status(launch_quant_fp8(x, q, scale, rows, cfg->hidden, stream));
+}
+
+int moe_quantize_mx(const moe_config* cfg, int64_t rows, const void* x, uint8_t* q, uint8_t* scale,
+                    hipStream_t stream) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (cfg->dtype != MOE_DTYPE_MXFP4) return MOE_ERR_INVALID_ARG;
+    if (rows < 0 || rows > INT32_MAX) return MOE_ERR_INVALID_ARG;
+    if (rows == 0) return MOE_OK;
+    if (!x || !q || !scale) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(q)) return MOE_ERR_MISALIGNED;
+    return hip_status(launch_quant_mx(x, q, scale, rows, cfg->hidden, stream));
 }
 
 int moe_expert_load(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int64_t* load, hipStream_t stream) {

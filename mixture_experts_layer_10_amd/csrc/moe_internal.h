@@ -50,17 +50,17 @@ struct GemmArgs {
     // shared-expert rows (token t = row).
     const void* A;            // routed-row source
     const void* A_shared;     // shared-row source (may equal A)
-    const float* A_scale;     // FP8: [rows, K/128] scales of A (routed source)
-    const float* A_scale_shared;
+    const void* A_scale;      // FP8: float [rows, K/128]; MXFP4: E8M0 bytes [rows, K/32]
+    const void* A_scale_shared;
     const int32_t* perm;      // gather: token = perm[row] / topk
     int gather;
     int topk;
     // B operand: [n_local, N_B, K] routed weights, [N_B, K] shared weights.
     const void* B;
     const void* B_shared;
-    const float* B_scale;     // FP8: [n_local, N_B/128, K/128]
-    const float* B_scale_shared;
-    int64_t b_stride;         // elements between routed experts
+    const void* B_scale;      // FP8: float [n_local, N_B/128, K/128]; MXFP4: bytes [n_local, N_B, K/32]
+    const void* B_scale_shared;
+    int64_t b_stride;         // elements between routed experts (MXFP4: bytes)
     // Groups: rows of routed group g are offsets[g] .. offsets[g+1]-1;
     // group n_local (if has_shared) has T rows.
     const int32_t* offsets;   // [n_local + 1], or null for a single dense group
@@ -72,8 +72,8 @@ struct GemmArgs {
     // Outputs
     void* C;                  // routed rows [rows, ldc]
     void* C_shared;           // shared rows [T, ldc]
-    float* C_scale;           // FP8 SWIGLU: [rows, N/128]
-    float* C_scale_shared;
+    void* C_scale;            // SWIGLU, FP8: float [rows, N/128]; MXFP4: E8M0 bytes [rows, N/32]
+    void* C_scale_shared;
     int ldc;
     const float* bias;        // PLAIN fp32 out: per-column bias or null
     int out_f32;              // PLAIN: 1 -> fp32 output, 0 -> bf16 output
@@ -109,6 +109,11 @@ hipError_t launch_gemm_big(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStr
 hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* q, float* scale, int64_t rows, int cols, hipStream_t s);
 GemmPlan plan_gemm_fp8(Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N);
 hipError_t launch_gemm_fp8(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
+
+// --- FP4 (MX) weights: activation quantisation and the scaled-MFMA GEMM -----
+hipError_t launch_quant_mx(const void* x_bf16, uint8_t* q, uint8_t* scale, int64_t rows, int cols, hipStream_t s);
+GemmPlan plan_gemm_mx(Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N);
+hipError_t launch_gemm_mx(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
 
 // --- expert load statistics and placement -----------------------------------
 hipError_t launch_expert_load(const int32_t* ids, int64_t n, int E, int64_t* load, hipStream_t s);

@@ -9,7 +9,11 @@ import mixture_experts_layer_10_amd as moe
 from oracle import moe_oracle as O
 from synth import make_inputs
 
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+# Layer-output tolerance, max |dy| / RMS(y): fp32 and bf16 as the carrier
+# types' rounding allows; fp8 and mxfp4 both quantise x and h to e4m3 on both
+# sides (the oracle models it), so only accumulation order and the rare
+# e4m3 code of h that lands one step apart remain.
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "mxfp4": 6e-2}
 
 
 def say(*a):

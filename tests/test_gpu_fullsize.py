@@ -22,7 +22,7 @@ from gpu_helpers import TOL, host, say
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["ep8_decode_bf16", "full_decode_bf16", "full_prefill_bf16", "fp8_skew"]
+FULL = ["ep8_decode_bf16", "full_decode_bf16", "full_prefill_bf16", "fp8_skew", "full_decode_mxfp4"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -195,6 +195,17 @@ LAYER_CASES = {
     # fp8 64-row tiles on 8 wavefronts (routed, ~57 rows per expert) and
     # 128-row tiles (shared expert, 600 rows)
     "small_fp8_bm64_bm128": lambda: _small(dtype="fp8", T=600, score_bias="zero"),
+    # FP4 (MX) weights: 32-row tiles (~14 rows per expert), 64-row tiles on 8
+    # wavefronts (~56 rows per expert; shared expert 600 rows), a local share
+    # with a wider layer, capacity drops, one token, and the full-decode shape
+    "small_mxfp4": lambda: _small(dtype="mxfp4", T=150, score_bias="zero"),
+    "small_mxfp4_bm64": lambda: _small(dtype="mxfp4", T=600),
+    "small_mxfp4_share_wide": lambda: _small(dtype="mxfp4", T=90, expert_begin=8, expert_end=40, inter=512,
+                                             shared_inter=256, hidden=1024),
+    "small_mxfp4_capacity": lambda: _small(dtype="mxfp4", T=300, capacity_factor=1.25, router_bias="zipf1.1",
+                                           score_bias="zero"),
+    "small_mxfp4_one_token": lambda: _small(dtype="mxfp4", T=1),
+    "full_decode_mxfp4_T40": lambda: workload("full_decode_mxfp4", T=40),
 }
 
 
@@ -228,7 +239,7 @@ def test_layer_stages_match_oracle(name):
         slack = 2.0 ** -7 * np.abs(want) if w["dtype"] != "f32" else 0.0
         rms = math.sqrt(float(np.mean(want * want)))
         row_err = np.max(np.maximum(np.abs(got - want) - slack, 0.0), axis=1) / rms
-        if w["dtype"] == "fp8":
+        if w["dtype"] in ("fp8", "mxfp4"):
             # h is requantised to e4m3 on both sides; where GPU and oracle h
             # differ by accumulation rounding, a code can land one e4m3 step
             # (1/8 to 1/16 relative) apart, moving that row by one step of one
@@ -283,6 +294,34 @@ def test_quantize_fp8_bit_exact(rows, H):
     want_q, want_s = O.quantize_fp8_rows(x.float().numpy())
     got_q = q.cpu().numpy()
     assert np.array_equal(host(sc).view(np.int32), want_s.view(np.int32))
+    assert not np.any((got_q & 0x7F) == 0x7F)             # no NaN codes
+    assert np.array_equal(O.e4m3_decode(got_q), want_q)
+
+
+# ---------------------------------------------------------------------------
+# MX activation quantiser: codes and E8M0 scales bit for bit
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,H", [(1, 256), (37, 512), (300, 7168), (4099, 1024)])
+def test_quantize_mx_bit_exact(rows, H):
+    say("quantize_mx case", rows, H)
+    cfg = moe.make_config(H, 8, 2, 256, dtype="mxfp4", n_group=1, topk_group=1, score_fn="softmax")
+    rng = np.random.default_rng(rows * 5 + H)
+    x = _quant_input(rows, H, rng)
+    if rows > 8:
+        xf = x.float()
+        xf[7, :32] = 0.0
+        xf[7, 0], xf[7, 1] = 1.0625, -1.1875                  # e4m3 midpoints after scaling: ties to even
+        xf[7, 32:64] = torch.linspace(-1.99, 1.99, 32)        # saturates at 448 * 2**X
+        xf[8, :] = 2.0 ** -133                                # bf16 subnormals: exponent clamped at -127
+        x = xf.to(torch.bfloat16)
+    q = torch.full((rows, H), 0xAA, dtype=torch.uint8, device="cuda")
+    sc = torch.full((rows, H // 32), 0x55, dtype=torch.uint8, device="cuda")
+    moe.moe_quantize_mx(cfg, x.cuda(), q, sc)
+    torch.cuda.synchronize()
+    want_q, want_s = O.quantize_mx_rows(x.float().numpy())
+    got_q = q.cpu().numpy()
+    assert np.array_equal(sc.cpu().numpy(), want_s)
     assert not np.any((got_q & 0x7F) == 0x7F)             # no NaN codes
     assert np.array_equal(O.e4m3_decode(got_q), want_q)
 

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert moe.lib().moe_abi_version() == moe.ABI_VERSION == 1
+    assert moe.lib().moe_abi_version() == moe.ABI_VERSION == 2
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert moe.status_string(st) not in ("", "unknown status")
     assert moe.status_string(-99) == "unknown status"
@@ -57,6 +57,10 @@ def _good(**kw):
     (dict(inter=2000), B.ERR_UNSUPPORTED),
     (dict(top_k=17, topk_group=8), B.ERR_UNSUPPORTED),
     (dict(n_experts=1024, expert_end=32), B.ERR_UNSUPPORTED),
+    (dict(dtype="mxfp4"), B.OK),
+    (dict(dtype="mxfp4", hidden=7168 + 128), B.ERR_UNSUPPORTED),   # FP4 GEMM: K chunks of 256
+    (dict(dtype="mxfp4", inter=2048 + 128), B.ERR_UNSUPPORTED),
+    (dict(dtype="mxfp4", shared_inter=384), B.ERR_UNSUPPORTED),
 ])
 def test_validate_config(kw, status):
     assert moe.validate_config(_good(**kw)) == status
@@ -64,7 +68,7 @@ def test_validate_config(kw, status):
 
 def test_abi_mismatch_and_null_config():
     c = _good()
-    c.abi_version = 2
+    c.abi_version = moe.ABI_VERSION + 1
     assert moe.validate_config(c) == B.ERR_ABI_MISMATCH
     assert moe.lib().moe_validate_config(None) == B.ERR_INVALID_ARG
 
@@ -108,6 +112,22 @@ def test_stage_calls_reject_before_launch():
     W.w13 = W.w2 = W.shared_w13 = W.shared_w2 = FAKE
     assert L.moe_expert_ffn(cp, 4, FAKE, FAKE, FAKE, ctypes.byref(W), FAKE, None, FAKE, need, None) == \
         B.ERR_INVALID_ARG
+    # quantised layers need their weight scales, MX scales 8-byte aligned
+    mx = _good(dtype="mxfp4")
+    mxp = ctypes.byref(mx)
+    need_mx = moe.workspace_bytes(mx, 4)
+    Wm = B.Weights()
+    Wm.w13 = Wm.w2 = Wm.shared_w13 = Wm.shared_w2 = FAKE
+    assert L.moe_expert_ffn(mxp, 4, FAKE, FAKE, FAKE, ctypes.byref(Wm), FAKE, FAKE, FAKE, need_mx, None) == \
+        B.ERR_INVALID_ARG
+    Wm.w13_scale = Wm.w2_scale = Wm.shared_w13_scale = FAKE
+    Wm.shared_w2_scale = FAKE + 4
+    assert L.moe_expert_ffn(mxp, 4, FAKE, FAKE, FAKE, ctypes.byref(Wm), FAKE, FAKE, FAKE, need_mx, None) == \
+        B.ERR_INVALID_ARG
+    # the MX quantiser takes MXFP4 configs only
+    assert L.moe_quantize_mx(cp, 4, FAKE, FAKE, FAKE, None) == B.ERR_INVALID_ARG
+    assert L.moe_quantize_mx(mxp, 4, FAKE + 8, FAKE, FAKE, None) == B.ERR_MISALIGNED
+    assert L.moe_quantize_mx(mxp, 0, None, None, None, None) == B.OK
     # invalid config is reported by every entry point
     bad = _good(n_group=7)
     assert L.moe_forward(ctypes.byref(bad), 4, FAKE, FAKE, None, None, ctypes.byref(W), FAKE, None, None,
