@@ -50,7 +50,8 @@ def parse():
 # Kernel sources whose code a stored traffic measurement belongs to.
 KERNEL_SOURCES = {"bf16": ["gemm.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
                   "f32": ["gemm.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
-                  "fp8": ["gemm_fp8.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"]}
+                  "fp8": ["gemm_fp8.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
+                  "mxfp4": ["gemm_mx.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"]}
 
 
 def kernel_source_hash(dtype):
@@ -101,19 +102,25 @@ def stage_bytes_flops(w, counts, stage):
 
     GroupGEMM I/O model g*(m*k + n*k + m*n) elements and 2*g*m*k*n FLOPs
     (Perplexity, "Roofline > GroupGEMM"), with m_i the rows of expert i, only
-    experts with rows counted, each term at its stored element size."""
+    experts with rows counted, each term at its stored element size:
+    weights wb bytes per element (fp8: 1, the 128x128 block scales
+    negligible; mxfp4: half a byte plus one scale byte per 32), quantised
+    activations ab (e4m3 plus a 4-byte scale per 128 or a 1-byte scale per
+    32: 1 + 1/32 either way), expert output rows bf16 (fp32 for f32)."""
     H, I, Is, T = w["hidden"], w["inter"], w["shared_inter"], w["T"]
-    eb = {"bf16": 2, "f32": 4, "fp8": 1}[w["dtype"]]
+    wb = {"bf16": 2, "f32": 4, "fp8": 1, "mxfp4": 0.5 + 1 / 32}[w["dtype"]]
+    ab = {"bf16": 2, "f32": 4, "fp8": 1 + 1 / 32, "mxfp4": 1 + 1 / 32}[w["dtype"]]
+    ob = 4 if w["dtype"] == "f32" else 2
     R = int(counts.sum())
     active = int((counts > 0).sum())
     if stage == "gate_up":
-        return (R * H + active * 2 * I * H + R * I) * eb, 2.0 * R * H * 2 * I
+        return (R * H + R * I) * ab + active * 2 * I * H * wb, 2.0 * R * H * 2 * I
     if stage == "down":
-        return (R * I + active * H * I) * eb + R * H * max(eb, 2), 2.0 * R * I * H
+        return R * I * ab + active * H * I * wb + R * H * ob, 2.0 * R * I * H
     if stage == "shared_gate_up":
-        return (T * H + 2 * Is * H + T * Is) * eb, 2.0 * T * H * 2 * Is
+        return (T * H + T * Is) * ab + 2 * Is * H * wb, 2.0 * T * H * 2 * Is
     if stage == "shared_down":
-        return (T * Is + H * Is) * eb + T * H * 4, 2.0 * T * Is * H
+        return T * Is * ab + H * Is * wb + T * H * 4, 2.0 * T * Is * H
     raise ValueError(stage)
 
 
@@ -134,7 +141,9 @@ def cpu_baseline(w, inp, sample, min_seconds=10.0):
         if t is None:
             return None
         t = t.detach().cpu()
-        return t.view(torch.uint8).numpy() if t.dtype == torch.float8_e4m3fn else t.float().numpy()
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).numpy()
+        return t.numpy() if t.dtype == torch.uint8 else t.float().numpy()
 
     cfg = O.Config.from_workload(w)
     S = min(sample, w["T"])
@@ -245,7 +254,9 @@ def main():
     if graphed:
         dom_ms, dom_n = prof[dom]
     t_dom = dom_ms / dom_n * 1e-3
-    peak_mfma = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "f32": PEAK_F32_TFLOPS}[w["dtype"]]
+    # e4m3 x E2M1 runs at the fp8 rate of the scaled MFMA
+    peak_mfma = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "mxfp4": PEAK_FP8_TFLOPS,
+                 "f32": PEAK_F32_TFLOPS}[w["dtype"]]
     ridge = peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
     if flops / byts < ridge:
         roof = {"bound": "hbm", "achieved": byts / t_dom / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -253,7 +264,8 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": peak_mfma, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = stored_traffic(dom, a.config, w["dtype"])
-    roof["kernel"] = f"gemm_kernel ({dom})"
+    family = {"fp8": "gemm_fp8_kernel", "mxfp4": "gemm_mx_kernel"}.get(w["dtype"], "gemm_kernel / gemm_big_kernel")
+    roof["kernel"] = f"{family} ({dom})"
     roof["kernel_ms"] = t_dom * 1e3
     roof["kernel_launches_timed"] = dom_n
     roof["kernel_time_source"] = "untimed per-stage pass" if graphed else "timed region"

@@ -32,9 +32,6 @@
 namespace moe {
 namespace {
 
-constexpr int kChunk = 256;            // K per chunk: two MFMA K-steps
-constexpr int kRowA = 256;             // LDS bytes per A row per chunk
-constexpr int kRowG = kRowA / 16;      // 16-byte granules per A row per chunk
 constexpr int kBlk = 32;               // MX block (elements per scale)
 typedef int i32x4v __attribute__((ext_vector_type(4)));
 
@@ -56,6 +53,19 @@ __device__ __forceinline__ int mx_exponent(float m) {
 
 // 2**-X as a float for X in [-127, 119] (always a normal number).
 __device__ __forceinline__ float mx_inv_scale(int X) { return __uint_as_float(static_cast<uint32_t>(127 - X) << 23); }
+
+// Workgroup barrier of the LDS double buffer: waits for this wavefront's LDS
+// accesses (lgkmcnt 0) but not for its global loads (vmcnt left at its
+// maximum), so the weight and activation loads of the chunks ahead stay in
+// flight across it; __syncthreads would drain them every chunk.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // vmcnt 63, expcnt 7, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 // ---- x -> MX e4m3: one workgroup per row, 4 lanes per 32-column block ------
 __global__ __launch_bounds__(256) void quant_mx_kernel(const uint16_t* x, uint8_t* q, uint8_t* scale, int cols) {
@@ -88,23 +98,46 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const uint16_t* x, uint8_
 // ---- K5/K6 with FP4 weights ---------------------------------------------------
 // NW wavefronts split the tile's 256 weight rows: each holds NF = 16 / NW
 // fragments of 16 rows (SWIGLU: half gate, half up rows of the same h
-// columns).
-template <Epi EPI, int BM, int NW = 4>
-__global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm_mx_kernel(GemmArgs a, int n_tiles) {
+// columns). A chunk is CK elements of K: KH = CK / 128 MFMA steps, CK / 2
+// bytes of each weight row. Weights go straight from HBM into VGPRs PD chunks
+// ahead of use; the activation tile goes HBM/L2 -> VGPRs one chunk ahead and
+// VGPRs -> LDS (double-buffered) at the end of the chunk before its use.
+template <int N>
+struct Bytes {                                          // N scale bytes held as N / 4 dwords
+    uint32_t w[N / 4];
+};
+template <int N>
+__device__ __forceinline__ Bytes<N> ld_bytes(const unsigned char* p) {
+    Bytes<N> b;
+    if constexpr (N == 16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        b.w[0] = v.x; b.w[1] = v.y; b.w[2] = v.z; b.w[3] = v.w;
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        b.w[0] = v.x; b.w[1] = v.y;
+    }
+    return b;
+}
+
+template <Epi EPI, int BM, int NW, int CK, int PD, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n_tiles) {
     constexpr int NT = NW * 64;
     constexpr int NF = 16 / NW;                        // 16-row fragments per wavefront
     constexpr int NRF = BM / 16;
-    constexpr int ROWS_PER_PASS = NT / kRowG;          // 16 or 32
+    constexpr int KH = CK / 128;                       // MFMA K-steps per chunk
+    constexpr int ROWB = CK;                           // LDS bytes per A row per chunk (e4m3)
+    constexpr int ROWG = CK / 16;                      // 16-byte granules per A row per chunk
+    constexpr int SB = CK / kBlk;                      // scale bytes per row per chunk
+    constexpr int ROWS_PER_PASS = NT / ROWG;
     constexpr int PASSES = BM / ROWS_PER_PASS;
-    constexpr int PD = 1;                              // weight chunks in flight beyond the current one
-    constexpr int NB = PD + 1;
-    constexpr int APD = 2;
-    constexpr int U = 2;                               // steps per unrolled loop body (NB and 2 LDS buffers)
+    constexpr int NB = PD + 1;                         // weight register buffers
+    constexpr int U = NB;                              // steps per unrolled body: every buffer index static
     static_assert(BM % ROWS_PER_PASS == 0, "tile rows");
     static_assert(BM <= NT, "one activation-scale loader per tile row");
+    static_assert(KH == 2 || KH == 4, "chunk of 256 or 512");
 
-    __shared__ __attribute__((aligned(16))) unsigned char s_a[2][BM * kRowA];
-    __shared__ __attribute__((aligned(16))) uint2 s_sa[2][BM];     // 8 scale bytes per row per chunk
+    __shared__ __attribute__((aligned(16))) unsigned char s_a[2][BM * ROWB];
+    __shared__ __attribute__((aligned(16))) unsigned char s_sa[2][BM * SB];
     constexpr int CPW = 16 * (NF / 2);                              // SWIGLU: h columns per wavefront
     constexpr int WPB = CPW >= kBlk ? 1 : kBlk / CPW;               // wavefronts per 32-column block
     __shared__ float s_amax[WPB > 1 ? NW : 1][WPB > 1 ? BM : 1];
@@ -120,10 +153,12 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
     const int row0 = tl.row0, m0 = tl.m0, rows = tl.rows;
     const int nrf = (rows + 15) >> 4;
     const int K = a.K;
-    const int nch = K / kChunk;
+    const int nch = K / CK;
     const int kb = K / kBlk;                           // scale bytes per row
 
-    // ---- weights: packed E2M1 rows (K/2 bytes) and E8M0 scales (K/32 bytes)
+    // ---- weights: packed E2M1 rows (K/2 bytes) and E8M0 scales (K/32 bytes).
+    // Bases are workgroup-uniform and offsets 32-bit, so the loads take the
+    // scalar-base form and no 64-bit address per load sits in VGPRs.
     const int nb_rows = EPI == Epi::SWIGLU ? 2 * a.inter : a.N;
     const unsigned char* Bg = shared ? static_cast<const unsigned char*>(a.B_shared)
                                      : static_cast<const unsigned char*>(a.B) + static_cast<int64_t>(g) * a.b_stride;
@@ -146,9 +181,9 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
     }
 
     // ---- activations: gathered e4m3 rows and their scale bytes ------------
-    const int aj = tid % kRowG, ar = tid / kRowG;
-    const unsigned char* Abase = static_cast<const unsigned char*>(shared ? a.A_shared : a.A) + aj * 16;
-    const unsigned char* Ascale = static_cast<const unsigned char*>(shared ? a.A_scale_shared : a.A_scale);
+    const int aj = tid % ROWG, ar = tid / ROWG;
+    const unsigned char* Ag = static_cast<const unsigned char*>(shared ? a.A_shared : a.A);
+    const unsigned char* Asg = static_cast<const unsigned char*>(shared ? a.A_scale_shared : a.A_scale);
     auto src_row = [&](int r) -> uint32_t {
         r = r < rows ? r : rows - 1;
         if (shared) return m0 + r;
@@ -157,16 +192,12 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
     };
     uint32_t aoff[PASSES];
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) aoff[i] = src_row(ar + i * ROWS_PER_PASS) * static_cast<uint32_t>(K);
-    const unsigned char* sa_src = Ascale + (tid < BM ? static_cast<int64_t>(src_row(tid)) * kb : 0);
+    for (int i = 0; i < PASSES; ++i) aoff[i] = src_row(ar + i * ROWS_PER_PASS) * static_cast<uint32_t>(K) + aj * 16;
+    const uint32_t sao = tid < BM ? src_row(tid) * static_cast<uint32_t>(kb) : 0u;
     // LDS: row r's granule j sits at j ^ (r & 15): the 16 rows of a fragment
     // read 16 different granule slots, so the 64 lanes' reads spread over all banks.
-    const int a_st = ar * kRowA + ((aj ^ (ar & 15)) * 16);
-    int a_ld[2][2];                                    // [K half][16-byte part]
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) a_ld[h][s] = lr * kRowA + (((8 * h + 4 * s + lq) ^ lr) * 16);
+    const int a_st = ar * ROWB + ((aj ^ (ar & 15)) * 16);
+    const int a_ld = lr * ROWB;
 
     f32x4 acc[NRF][NF];
 #pragma unroll
@@ -174,83 +205,83 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
 #pragma unroll
         for (int f = 0; f < NF; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    i32x4v breg[NB][NF][2];
-    uint2 bsreg[NB][NF];
-    vec16 areg[APD][PASSES];
-    uint2 sareg[APD];
+    i32x4v breg[NB][NF][KH];
+    Bytes<SB> bsreg[NB][NF];
+    vec16 areg[PASSES];
+    Bytes<SB> sareg;
     const int last = nch - 1;
 
-    auto load_b = [&](i32x4v (&dst)[NF][2], uint2 (&ds)[NF], int c) __attribute__((always_inline)) {
+    auto load_b = [&](i32x4v (&dst)[NF][KH], Bytes<SB> (&ds)[NF], int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            const unsigned char* p = Bg + boff[f] + static_cast<int64_t>(c) * (kChunk / 2);
-            dst[f][0] = *reinterpret_cast<const i32x4v*>(p);
-            dst[f][1] = *reinterpret_cast<const i32x4v*>(p + 64);
-            ds[f] = *reinterpret_cast<const uint2*>(Sg + soff[f] + c * (kChunk / kBlk));
+            const uint32_t o = boff[f] + static_cast<uint32_t>(c) * (CK / 2);
+#pragma unroll
+            for (int h = 0; h < KH; ++h) dst[f][h] = *reinterpret_cast<const i32x4v*>(Bg + (o + h * 64));
+            ds[f] = ld_bytes<SB>(Sg + (soff[f] + static_cast<uint32_t>(c) * SB));
         }
     };
-    auto load_a = [&](vec16 (&dst)[PASSES], uint2& ds, int c) __attribute__((always_inline)) {
+    auto load_a = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < PASSES; ++i) dst[i] = ld16(Abase + aoff[i] + static_cast<int64_t>(c) * kChunk);
-        if (tid < BM) ds = *reinterpret_cast<const uint2*>(sa_src + c * (kChunk / kBlk));
+        for (int i = 0; i < PASSES; ++i) areg[i] = ld16(Ag + (aoff[i] + static_cast<uint32_t>(c) * CK));
+        if (tid < BM) sareg = ld_bytes<SB>(Asg + (sao + static_cast<uint32_t>(c) * SB));
     };
-    auto store_a = [&](const vec16 (&src)[PASSES], uint2 ds, int buf) __attribute__((always_inline)) {
+    auto store_a = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < PASSES; ++i) st16(&s_a[buf][a_st + i * ROWS_PER_PASS * kRowA], src[i]);
-        if (tid < BM) s_sa[buf][tid] = ds;
+        for (int i = 0; i < PASSES; ++i) st16(&s_a[buf][a_st + i * ROWS_PER_PASS * ROWB], areg[i]);
+        if (tid < BM) {
+            if constexpr (SB == 16)
+                *reinterpret_cast<uint4*>(&s_sa[buf][tid * SB]) = make_uint4(sareg.w[0], sareg.w[1], sareg.w[2], sareg.w[3]);
+            else
+                *reinterpret_cast<uint2*>(&s_sa[buf][tid * SB]) = make_uint2(sareg.w[0], sareg.w[1]);
+        }
     };
-    auto compute = [&](const i32x4v (&bv)[NF][2], const uint2 (&bs)[NF], int buf) __attribute__((always_inline)) {
+    auto compute = [&](const i32x4v (&bv)[NF][KH], const Bytes<SB> (&bs)[NF], int buf) __attribute__((always_inline)) {
         const unsigned char* src = s_a[buf];
-        const unsigned char* ssa = reinterpret_cast<const unsigned char*>(s_sa[buf]);
-        // this lane's weight-scale byte for each K half: byte lq (half 0) and 4 + lq (half 1)
-        int sb[NF][2];
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            sb[f][0] = static_cast<int>(bs[f].x >> (8 * lq));
-            sb[f][1] = static_cast<int>(bs[f].y >> (8 * lq));
-        }
+        const unsigned char* ssa = s_sa[buf];
 #pragma unroll
         for (int i = 0; i < NRF; ++i) {
             if (i == 0 || i < nrf) {
-                const unsigned char* ri = src + i * 16 * kRowA;
-                const int arow = (i * 16 + lr) * 8;
+                const unsigned char* ri = src + i * 16 * ROWB + a_ld;
+                const int arow = (i * 16 + lr) * SB;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const vec16 lo = ld16(ri + a_ld[h][0]);
-                    const vec16 hi = ld16(ri + a_ld[h][1]);
+                for (int h = 0; h < KH; ++h) {
+                    // this lane's e4m3 bytes: K = 16 lq .. and 64 + 16 lq .. of step h
+                    const vec16 lo = ld16(ri + (((8 * h + lq) ^ lr) * 16));
+                    const vec16 hi = ld16(ri + (((8 * h + 4 + lq) ^ lr) * 16));
                     const i32x8 av = {static_cast<int>(lo.w[0]), static_cast<int>(lo.w[1]), static_cast<int>(lo.w[2]),
                                       static_cast<int>(lo.w[3]), static_cast<int>(hi.w[0]), static_cast<int>(hi.w[1]),
                                       static_cast<int>(hi.w[2]), static_cast<int>(hi.w[3])};
-                    const int sa = ssa[arow + 4 * h + lq];
+                    const int sa = ssa[arow + 4 * h + lq];           // scale of K block 4h + lq
 #pragma unroll
                     for (int f = 0; f < NF; ++f) {
                         const i32x4v b4 = bv[f][h];
                         const i32x8 b8 = {b4[0], b4[1], b4[2], b4[3], 0, 0, 0, 0};
-                        acc[i][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b8, acc[i][f], 0, 4, 0, sa, 0,
-                                                                                    sb[f][h]);
+                        acc[i][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, b8, acc[i][f], 0, 4, 0, sa, 0, static_cast<int>(bs[f].w[h] >> (8 * lq)));
                     }
                 }
             }
         }
     };
 
-    // ---- main loop: loads of chunk c + APD (A) and c + PD (B) in flight
-    // while chunk c is multiplied; the A tile is double-buffered in LDS ------
+    // ---- main loop. Per chunk c: the activations of c + 1 are loaded first
+    // and the weights of c + PD after them, so that waiting for the former
+    // (to stage them into LDS at the end of the chunk) never waits for the
+    // weights just issued; chunk c is multiplied in between. ----------------
     auto step = [&](auto uc, int c) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
-        load_a(areg[u % APD], sareg[u % APD], min(c + APD, last));
+        load_a(min(c + 1, last));
         load_b(breg[(u + PD) % NB], bsreg[(u + PD) % NB], min(c + PD, last));
-        compute(breg[u % NB], bsreg[u % NB], u & 1);
-        store_a(areg[(u + 1) % APD], sareg[(u + 1) % APD], (u + 1) & 1);
-        __syncthreads();
+        compute(breg[u % NB], bsreg[u % NB], c & 1);
+        store_a((c + 1) & 1);
+        lds_barrier();
     };
     if (nch > 0) {
-#pragma unroll
-        for (int p = 0; p < APD; ++p) load_a(areg[p], sareg[p], min(p, last));
+        load_a(0);
 #pragma unroll
         for (int p = 0; p < PD; ++p) load_b(breg[p], bsreg[p], min(p, last));
-        store_a(areg[0], sareg[0], 0);
-        __syncthreads();
+        store_a(0);
+        lds_barrier();
     }
     int c = 0;
     for (; c + U <= nch; c += U) {
@@ -258,7 +289,9 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
             (step(std::integral_constant<int, I>{}, c + I), ...);
         }(std::make_integer_sequence<int, U>{});
     }
-    if (c < nch) step(std::integral_constant<int, 0>{}, c);
+    [&]<int... I>(std::integer_sequence<int, I...>) {           // at most U - 1 steps remain
+        ((c + I < nch ? step(std::integral_constant<int, I>{}, c + I) : void()), ...);
+    }(std::make_integer_sequence<int, U - 1>{});
 
     // ---- epilogue ------------------------------------------------------------
     const int64_t crow0 = shared ? m0 : static_cast<int64_t>(row0) + m0;
@@ -351,13 +384,18 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
     }
 }
 
+template <Epi EPI, int BM, int NW, int CK, int PD, int OCC>
+void launch_mx_one(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_mx_kernel<EPI, BM, NW, CK, PD, OCC>), dim3(static_cast<unsigned>(p.grid)), dim3(NW * 64), 0,
+                       s, a, p.n_tiles);
+}
+
 template <Epi EPI>
 hipError_t launch_mx_bm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(p.grid));
     if (p.nw == 4 && p.bm == 32) {
-        hipLaunchKernelGGL((gemm_mx_kernel<EPI, 32, 4>), grid, dim3(256), 0, s, a, p.n_tiles);
+        launch_mx_one<EPI, 32, 4, 256, 1, 2>(a, p, s);
     } else if (p.nw == 8 && p.bm == 64) {
-        hipLaunchKernelGGL((gemm_mx_kernel<EPI, 64, 8>), grid, dim3(512), 0, s, a, p.n_tiles);
+        launch_mx_one<EPI, 64, 8, 256, 1, 2>(a, p, s);
     } else {
         return hipErrorInvalidValue;
     }
@@ -379,8 +417,9 @@ GemmPlan plan_gemm_mx(Epi epi, int64_t rows_upper, int n_groups, int64_t expecte
     p.smajor = 0;
     p.big = 0;
     p.ksplit = 1;
-    // 32-row tiles on 4 wavefronts; 64-row tiles on 8 (two per SIMD), which
-    // halves each wavefront's share of the weight fragments and accumulators.
+    // 32-row tiles on 4 wavefronts, 64-row tiles on 8 (two per SIMD, each
+    // holding half the weight fragments); one chunk of weights in flight
+    // beyond the one being multiplied.
     p.bm = expected_rows_per_group <= 32 ? 32 : 64;
     p.nw = p.bm == 32 ? 4 : 8;
     const int cols = epi == Epi::SWIGLU ? 128 : 256;
@@ -392,7 +431,7 @@ GemmPlan plan_gemm_mx(Epi epi, int64_t rows_upper, int n_groups, int64_t expecte
 
 hipError_t launch_gemm_mx(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     if (p.grid == 0) return hipSuccess;
-    if (a.K % kChunk != 0) return hipErrorInvalidValue;
+    if (a.K % 256 != 0) return hipErrorInvalidValue;
     GemmArgs b = a;
     b.ksplit = 1;
     return epi == Epi::SWIGLU ? launch_mx_bm<Epi::SWIGLU>(b, p, s) : launch_mx_bm<Epi::PLAIN>(b, p, s);
