@@ -101,7 +101,11 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const uint16_t* x, uint8_
 // columns). A chunk is CK elements of K: KH = CK / 128 MFMA steps, CK / 2
 // bytes of each weight row. Weights go straight from HBM into VGPRs PD chunks
 // ahead of use; the activation tile goes HBM/L2 -> VGPRs one chunk ahead and
-// VGPRs -> LDS (double-buffered) at the end of the chunk before its use.
+// VGPRs -> LDS (double-buffered) at the end of the chunk before its use. The
+// weight scales of the tile's 256 rows (K/32 bytes each) are read once, at
+// the start, into LDS (dynamic shared memory, mx_scale_lds_bytes): read a few
+// bytes per row per chunk from global memory instead, their cache lines are
+// evicted by the streaming weights between chunks and fetched several times.
 template <int N>
 struct Bytes {                                          // N scale bytes held as N / 4 dwords
     uint32_t w[N / 4];
@@ -118,6 +122,11 @@ __device__ __forceinline__ Bytes<N> ld_bytes(const unsigned char* p) {
     }
     return b;
 }
+
+// Row stride of the staged weight scales: K/32 bytes plus 8, so that the 16
+// rows of a fragment fall in different LDS banks.
+__host__ __device__ constexpr int mx_scale_stride(int K) { return K / kBlk + 8; }
+__host__ __device__ constexpr int mx_scale_lds_bytes(int K) { return 256 * mx_scale_stride(K); }
 
 template <Epi EPI, int BM, int NW, int CK, int PD, int OCC>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n_tiles) {
@@ -141,6 +150,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n
     constexpr int CPW = 16 * (NF / 2);                              // SWIGLU: h columns per wavefront
     constexpr int WPB = CPW >= kBlk ? 1 : kBlk / CPW;               // wavefronts per 32-column block
     __shared__ float s_amax[WPB > 1 ? NW : 1][WPB > 1 ? BM : 1];
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_bs[];   // [256][kbp] weight scales
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -165,7 +175,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n
     const unsigned char* Sg = shared ? static_cast<const unsigned char*>(a.B_scale_shared)
                                      : static_cast<const unsigned char*>(a.B_scale) +
                                            static_cast<int64_t>(g) * nb_rows * kb;
-    uint32_t boff[NF], soff[NF];
+    const int kbp = mx_scale_stride(K);
+    uint32_t boff[NF];
+    int sb_ld[NF];                                     // LDS offset of this lane's row of weight scales
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         int brow;
@@ -177,8 +189,27 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n
             brow = brow < a.N ? brow : a.N - 1;
         }
         boff[f] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K / 2) + lq * 16;
-        soff[f] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(kb);
+        const int trow = EPI == Epi::SWIGLU ? (f < NF / 2 ? wave * (128 / NW) + 16 * f + lr
+                                                           : 128 + wave * (128 / NW) + 16 * (f - NF / 2) + lr)
+                                            : wave * (256 / NW) + 16 * f + lr;
+        sb_ld[f] = trow * kbp + lq;
     }
+    // Stage the tile's weight scales: tile row j is weight row
+    // (SWIGLU) nt*128 + j (gate) or inter + nt*128 + j - 128 (up), or
+    // (PLAIN) nt*256 + j clamped to N - 1; 8 bytes per load, consecutive
+    // threads on consecutive bytes of a row. Called once, after the first
+    // chunk's loads are issued and before the first barrier.
+    auto stage_scales = [&]() __attribute__((always_inline)) {
+        const int vpr = kb / 8;
+        for (int v = tid; v < 256 * vpr; v += NT) {
+            const int j = v / vpr, q = v - j * vpr;
+            int wrow;
+            if constexpr (EPI == Epi::SWIGLU) wrow = j < 128 ? nt * 128 + j : a.inter + nt * 128 + (j - 128);
+            else wrow = min(nt * 256 + j, a.N - 1);
+            const uint2 val = *reinterpret_cast<const uint2*>(Sg + (static_cast<uint32_t>(wrow) * kb + q * 8));
+            *reinterpret_cast<uint2*>(s_bs + j * kbp + q * 8) = val;
+        }
+    };
 
     // ---- activations: gathered e4m3 rows and their scale bytes ------------
     const int aj = tid % ROWG, ar = tid / ROWG;
@@ -206,18 +237,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n
         for (int f = 0; f < NF; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     i32x4v breg[NB][NF][KH];
-    Bytes<SB> bsreg[NB][NF];
     vec16 areg[PASSES];
     Bytes<SB> sareg;
     const int last = nch - 1;
 
-    auto load_b = [&](i32x4v (&dst)[NF][KH], Bytes<SB> (&ds)[NF], int c) __attribute__((always_inline)) {
+    auto load_b = [&](i32x4v (&dst)[NF][KH], int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
             const uint32_t o = boff[f] + static_cast<uint32_t>(c) * (CK / 2);
 #pragma unroll
             for (int h = 0; h < KH; ++h) dst[f][h] = *reinterpret_cast<const i32x4v*>(Bg + (o + h * 64));
-            ds[f] = ld_bytes<SB>(Sg + (soff[f] + static_cast<uint32_t>(c) * SB));
         }
     };
     auto load_a = [&](int c) __attribute__((always_inline)) {
@@ -235,9 +264,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n
                 *reinterpret_cast<uint2*>(&s_sa[buf][tid * SB]) = make_uint2(sareg.w[0], sareg.w[1]);
         }
     };
-    auto compute = [&](const i32x4v (&bv)[NF][KH], const Bytes<SB> (&bs)[NF], int buf) __attribute__((always_inline)) {
+    auto compute = [&](const i32x4v (&bv)[NF][KH], int c, int buf) __attribute__((always_inline)) {
         const unsigned char* src = s_a[buf];
         const unsigned char* ssa = s_sa[buf];
+        const unsigned char* sbs = s_bs + c * SB;
+        int sb[NF][KH];                                // weight scale of K block 4h + lq of this lane's row
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int h = 0; h < KH; ++h) sb[f][h] = sbs[sb_ld[f] + 4 * h];
 #pragma unroll
         for (int i = 0; i < NRF; ++i) {
             if (i == 0 || i < nrf) {
@@ -257,7 +292,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n
                         const i32x4v b4 = bv[f][h];
                         const i32x8 b8 = {b4[0], b4[1], b4[2], b4[3], 0, 0, 0, 0};
                         acc[i][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            av, b8, acc[i][f], 0, 4, 0, sa, 0, static_cast<int>(bs[f].w[h] >> (8 * lq)));
+                            av, b8, acc[i][f], 0, 4, 0, sa, 0, sb[f][h]);
                     }
                 }
             }
@@ -271,15 +306,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n
     auto step = [&](auto uc, int c) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         load_a(min(c + 1, last));
-        load_b(breg[(u + PD) % NB], bsreg[(u + PD) % NB], min(c + PD, last));
-        compute(breg[u % NB], bsreg[u % NB], c & 1);
+        load_b(breg[(u + PD) % NB], min(c + PD, last));
+        compute(breg[u % NB], c, c & 1);
         store_a((c + 1) & 1);
         lds_barrier();
     };
     if (nch > 0) {
         load_a(0);
 #pragma unroll
-        for (int p = 0; p < PD; ++p) load_b(breg[p], bsreg[p], min(p, last));
+        for (int p = 0; p < PD; ++p) load_b(breg[p], min(p, last));
+        stage_scales();
         store_a(0);
         lds_barrier();
     }
@@ -385,21 +421,26 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n
 }
 
 template <Epi EPI, int BM, int NW, int CK, int PD, int OCC>
-void launch_mx_one(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_mx_kernel<EPI, BM, NW, CK, PD, OCC>), dim3(static_cast<unsigned>(p.grid)), dim3(NW * 64), 0,
-                       s, a, p.n_tiles);
+hipError_t launch_mx_one(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    auto* kern = &gemm_mx_kernel<EPI, BM, NW, CK, PD, OCC>;
+    const int dyn = mx_scale_lds_bytes(a.K);
+    static int attr = 0;                       // dynamic LDS limit raised so far (per instantiation)
+    if (dyn > attr) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+        if (e != hipSuccess) return e;
+        attr = dyn;
+    }
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(p.grid)), dim3(NW * 64), static_cast<size_t>(dyn), s, a,
+                       p.n_tiles);
+    return hipGetLastError();
 }
 
 template <Epi EPI>
 hipError_t launch_mx_bm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
-    if (p.nw == 4 && p.bm == 32) {
-        launch_mx_one<EPI, 32, 4, 256, 1, 2>(a, p, s);
-    } else if (p.nw == 8 && p.bm == 64) {
-        launch_mx_one<EPI, 64, 8, 256, 1, 2>(a, p, s);
-    } else {
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    if (p.nw == 4 && p.bm == 32) return launch_mx_one<EPI, 32, 4, 256, 1, 2>(a, p, s);
+    if (p.nw == 8 && p.bm == 64) return launch_mx_one<EPI, 64, 8, 256, 1, 2>(a, p, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
