@@ -339,6 +339,262 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
     }
 }
 
+// ---- compute-bound shapes: 256 x 256 tiles staged through LDS -------------
+// For groups of a thousand rows and more (the shared expert at prefill-sized
+// batches) the weights are reused by many row tiles and the product is bound
+// by matrix throughput. The structure is the bf16 256 x 256 kernel's:
+//  * 8 wavefronts as 2 (rows) x 4 (weight rows), each 128 x 64 as 16 x 16
+//    fragments of v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales);
+//  * both operands HBM/L2 -> LDS by direct loads, K = 128 per stage (one
+//    128-byte line per row), two stages; the stage's 256 activation scales
+//    ride along in 4-byte direct loads;
+//  * one scale block per stage: the fragment's product is added to the
+//    accumulator times a_scale[row] * w_scale[block] (the weight block of a
+//    wavefront's gate, up or plain columns is uniform: scalar loads).
+constexpr int kBigKB = 128;                         // K (bytes) per stage
+constexpr int kBigRows = 256;
+constexpr int kBigStageB = 2 * kBigRows * kBigKB + kBigRows * 4;   // A, B, A scales
+constexpr int kBigStages = 2;
+
+__device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
+
+template <Epi EPI>
+__global__ __launch_bounds__(512, 1) void gemm_big_fp8_kernel(GemmArgs a, int n_tiles) {
+    constexpr int NW = 8, NT = 512;
+    constexpr int GRAN = kBigKB / 16;                  // 8 granules per row
+    constexpr int LOADS = kBigRows * GRAN / NT;        // 4 direct loads per operand per stage
+    constexpr int RPL = 64 / GRAN;                     // 8 rows per load instruction
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_ring[];
+    __shared__ float s_amax[4][kBigRows];              // SWIGLU epilogue: per-wave-column row amax
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    Tile tl;
+    if (!find_tile(a, n_tiles, kBigRows, tl, /*balanced=*/true)) return;
+    const int g = tl.g, nt = tl.nt;
+    const bool shared = tl.shared;
+    const int row0 = tl.row0, m0 = tl.m0, rows = tl.rows;
+    const int K = a.K;
+    const int nkb = K / kBigKB;
+    const int last = nkb - 1;
+
+    auto src_row = [&](int r) -> uint32_t {
+        r = r < rows ? r : rows - 1;
+        if (shared) return m0 + r;
+        if (a.gather) return static_cast<uint32_t>(a.perm[row0 + m0 + r] / a.topk);
+        return row0 + m0 + r;
+    };
+    // direct-load sources: instruction j of wavefront w fills tile rows
+    // (8 j + w) * 8 + lane / 8, granule slot lane % 8, with the granule the
+    // swizzle places there
+    const int lrow = lane / GRAN;
+    const unsigned char* Ag = static_cast<const unsigned char*>(shared ? a.A_shared : a.A);
+    uint32_t aoff[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int rs = (NW * j + wave) * RPL + lrow;
+        aoff[j] = src_row(rs) * static_cast<uint32_t>(K) + (((lane % GRAN) ^ big_swz(rs)) * 16);
+    }
+    const unsigned char* Bg = shared ? static_cast<const unsigned char*>(a.B_shared)
+                                     : static_cast<const unsigned char*>(a.B) + static_cast<int64_t>(g) * a.b_stride;
+    uint32_t boff[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int n = (NW * j + wave) * RPL + lrow;   // weight slot of the tile
+        int brow;
+        if constexpr (EPI == Epi::SWIGLU) {
+            // slots [64 w, 64 w + 64): 32 gate rows, then the 32 up rows of the same h columns
+            const int m = n & 63;
+            int col = nt * 128 + (n >> 6) * 32 + (m & 31);
+            col = col < a.inter ? col : a.inter - 1;
+            brow = m < 32 ? col : a.inter + col;
+        } else {
+            brow = nt * 256 + n;
+            brow = brow < a.N ? brow : a.N - 1;
+        }
+        boff[j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K) + (((lane % GRAN) ^ big_swz(n)) * 16);
+    }
+    const int kblocks = K / 128;
+    const float* Ascale = static_cast<const float*>(shared ? a.A_scale_shared : a.A_scale);
+    const uint32_t sa_off = wave < 4 ? src_row(wave * 64 + lane) * static_cast<uint32_t>(kblocks) : 0u;
+    // weight scales: one 128 x 128 block per wavefront and group
+    const int nb_rows = (EPI == Epi::SWIGLU ? 2 * a.inter : a.N) / 128;
+    const float* Sg = shared ? static_cast<const float*>(a.B_scale_shared)
+                             : static_cast<const float*>(a.B_scale) + static_cast<int64_t>(g) * nb_rows * kblocks;
+    const float* bsc0;
+    const float* bsc1;
+    if constexpr (EPI == Epi::SWIGLU) {
+        bsc0 = Sg + nt * kblocks;
+        bsc1 = Sg + (a.inter / 128 + nt) * kblocks;
+    } else {
+        bsc0 = bsc1 = Sg + min((nt * 256 + wn * 64) / 128, a.N / 128 - 1) * kblocks;
+    }
+
+    auto issue = [&](int kb, int slot) __attribute__((always_inline)) {
+        unsigned char* sa = s_ring + slot * kBigStageB;
+        unsigned char* sb = sa + kBigRows * kBigKB;
+        float* ss = reinterpret_cast<float*>(sb + kBigRows * kBigKB);
+        const uint32_t ko = static_cast<uint32_t>(kb) * kBigKB;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j)
+            __builtin_amdgcn_global_load_lds(Ag + (aoff[j] + ko),
+                                             (__attribute__((address_space(3))) void*)(sa + (NW * j + wave) * RPL * kBigKB),
+                                             16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j)
+            __builtin_amdgcn_global_load_lds(Bg + (boff[j] + ko),
+                                             (__attribute__((address_space(3))) void*)(sb + (NW * j + wave) * RPL * kBigKB),
+                                             16, 0, 0);
+        if (wave < 4)
+            __builtin_amdgcn_global_load_lds(Ascale + (sa_off + kb),
+                                             (__attribute__((address_space(3))) void*)(ss + wave * 64), 4, 0, 0);
+    };
+    auto sync = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0070);            // vmcnt 0, expcnt 7 (no wait), lgkmcnt 0
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // fragment reads: row r of a 16-row block, granules lq and 4 + lq
+    int fo[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) fo[h] = lr * kBigKB + (((4 * h + lq) ^ big_swz(lr)) * 16);
+    const int nrb = (rows + 15) >> 4;                  // 16-row blocks with data
+    const int nbw = min(max(nrb - wm * 8, 0), 8);      // of this wavefront's 8 (uniform)
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    issue(0, 0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        // stage kb has landed for every thread; stage kb - 1's slot is free
+        sync();
+        if (kb + 1 <= last) issue(kb + 1, (kb + 1) & 1);
+        const unsigned char* st = s_ring + (kb & 1) * kBigStageB;
+        const float* ss = reinterpret_cast<const float*>(st + 2 * kBigRows * kBigKB);
+        const float sb0 = bsc0[kb], sb1 = bsc1[kb];
+        i32x8v bfr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const unsigned char* p = st + kBigRows * kBigKB + (wn * 64 + j * 16) * kBigKB;
+            bfr[j] = ld32(p + fo[0], p + fo[1]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < nbw) {
+                const unsigned char* p = st + (wm * 128 + i * 16) * kBigKB;
+                const i32x8v af = ld32(p + fo[0], p + fo[1]);
+                const f32x4 sa = *reinterpret_cast<const f32x4*>(ss + wm * 128 + i * 16 + 4 * lq);
+                const f32x4 c0 = sa * sb0, c1 = sa * sb1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[j], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                                  0, 0, 0, 127, 0, 127);
+                    acc[i][j] += t * ((EPI == Epi::SWIGLU && j >= 2) ? c1 : c0);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue -----------------------------------------------------------
+    const int64_t crow0 = shared ? m0 : static_cast<int64_t>(row0) + m0;
+    if constexpr (EPI == Epi::SWIGLU) {
+        // h = silu(g) * u; the tile's 128 h columns are one 1x128 scale block:
+        // row amax over this wavefront's 32 columns, then across the 4
+        // wavefront columns in LDS
+        float h[8][2][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float m = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float gv = acc[i][j][v], uv = acc[i][j + 2][v];
+                    h[i][j][v] = gv / (1.0f + __expf(-gv)) * uv;
+                    m = fmaxf(m, fabsf(h[i][j][v]));
+                }
+#pragma unroll
+                for (int sft = 1; sft < 16; sft <<= 1) m = fmaxf(m, __shfl_xor(m, sft, 16));
+                if (lr == 0) s_amax[wn][wm * 128 + i * 16 + 4 * lq + v] = m;
+            }
+        __syncthreads();
+        uint8_t* Cq = static_cast<uint8_t*>(shared ? a.C_shared : a.C);
+        float* Cs = static_cast<float*>(shared ? a.C_scale_shared : a.C_scale);
+        const int nsb = a.N / 128;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < nbw) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = wm * 128 + i * 16 + 4 * lq + v;
+                    const float amax = fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
+                    const bool nz = amax > 0.0f;
+                    const float inv = nz ? fp8_inv_scale(amax) : 0.0f;
+                    if (r < rows) {
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const int col = nt * 128 + wn * 32 + j * 16 + lr;
+                            if (col < a.N) {
+                                const uint32_t code = nz ? (cvt2_e4m3(h[i][j][v] * inv, 0.0f) & 0xffu) : 0u;
+                                Cq[(crow0 + r) * a.ldc + col] = static_cast<uint8_t>(code);
+                            }
+                        }
+                        if (wn == 0 && lr == 0) Cs[(crow0 + r) * nsb + nt] = nz ? amax / 448.0f : 1.0f;
+                    }
+                }
+            }
+        }
+    } else {
+        unsigned char* Cb = static_cast<unsigned char*>(shared ? a.C_shared : a.C);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < nbw) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int col = nt * 256 + wn * 64 + j * 16 + lr;
+                    if (col < a.N) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int r = wm * 128 + i * 16 + 4 * lq + v;
+                            if (r < rows) {
+                                const int64_t off = (crow0 + r) * a.ldc + col;
+                                if (a.out_f32)
+                                    reinterpret_cast<float*>(Cb)[off] = acc[i][j][v];
+                                else
+                                    reinterpret_cast<uint16_t*>(Cb)[off] = f32_to_bf16_bits(acc[i][j][v]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <Epi EPI>
+hipError_t launch_big_fp8(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    constexpr int lds = kBigStages * kBigStageB;
+    static bool attr_set = false;              // once per instantiation
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_fp8_kernel<EPI>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((gemm_big_fp8_kernel<EPI>), dim3(static_cast<unsigned>(p.grid)), dim3(512), lds, s, a, p.n_tiles);
+    return hipGetLastError();
+}
+
 template <Epi EPI>
 hipError_t launch_fp8_bm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(p.grid));
@@ -384,10 +640,25 @@ GemmPlan plan_gemm_fp8(Epi epi, int64_t rows_upper, int n_groups, int64_t expect
     return p;
 }
 
+GemmPlan plan_gemm_fp8_big(Epi epi, int64_t rows_upper, int n_groups, int N) {
+    GemmPlan p;
+    p.bm = kBigRows;
+    p.nw = 8;
+    p.smajor = 0;
+    p.big = 1;
+    p.ksplit = 1;
+    const int cols = epi == Epi::SWIGLU ? 128 : 256;
+    p.n_tiles = (N + cols - 1) / cols;
+    const int64_t m_tiles = rows_upper / kBigRows + n_groups;
+    p.grid = ((m_tiles * p.n_tiles + 7) / 8) * 8;
+    return p;
+}
+
 hipError_t launch_gemm_fp8(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     if (p.grid == 0) return hipSuccess;
     GemmArgs b = a;
     b.ksplit = 1;
+    if (p.big) return epi == Epi::SWIGLU ? launch_big_fp8<Epi::SWIGLU>(b, p, s) : launch_big_fp8<Epi::PLAIN>(b, p, s);
     return epi == Epi::SWIGLU ? launch_fp8_bm<Epi::SWIGLU>(b, p, s) : launch_fp8_bm<Epi::PLAIN>(b, p, s);
 }
 

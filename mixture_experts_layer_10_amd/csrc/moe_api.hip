@@ -332,9 +332,11 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
 }
 
 // The shared expert is one dense group of T rows: from 1024 rows on it is
-// compute-bound, and the 256 x 256 LDS-pipelined tiles run it at about 1.4x
-// the rate of the bandwidth-oriented tiles (measured at T = 2048).
-bool shared_big_tiles(const moe_config* c, int64_t T) { return c->dtype == MOE_DTYPE_BF16 && T >= 1024; }
+// compute-bound, and the 256 x 256 LDS-pipelined tiles (bf16, fp8) run it
+// faster than the bandwidth-oriented tiles (bf16: 1.4x at T = 2048).
+bool shared_big_tiles(const moe_config* c, int64_t T) {
+    return (c->dtype == MOE_DTYPE_BF16 || c->dtype == MOE_DTYPE_FP8) && T >= 1024;
+}
 
 // Shared expert: every token, a single group (no schedule needed).
 hipError_t do_shared_ffn(const moe_config* c, int64_t T, const void* x, const moe_weights* wt, void* shared_out,
@@ -359,7 +361,9 @@ hipError_t do_shared_ffn(const moe_config* c, int64_t T, const void* x, const mo
         s1.A_scale = s1.A_scale_shared = at<void>(ws, L.xs);
         s1.B_scale = s1.B_scale_shared = wt->shared_w13_scale;
         s1.C_scale = s1.C_scale_shared = at<void>(ws, L.hs_shared);
-        const GemmPlan q1 = plan_quantised(c, Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
+        const bool bigq = c->dtype == MOE_DTYPE_FP8 && shared_big_tiles(c, T);
+        const GemmPlan q1 = bigq ? plan_gemm_fp8_big(Epi::SWIGLU, T, 1, static_cast<int>(Is))
+                                 : plan_quantised(c, Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
         {
             StageTimer tm(MOE_STAGE_SHARED_GATE_UP, s);
             if ((e = launch_quantised(c, Epi::SWIGLU, s1, q1, s)) != hipSuccess) return e;
@@ -376,7 +380,8 @@ hipError_t do_shared_ffn(const moe_config* c, int64_t T, const void* x, const mo
         s2.C_scale = s2.C_scale_shared = nullptr;
         s2.ldc = static_cast<int>(H);
         s2.out_f32 = 1;
-        const GemmPlan q2 = plan_quantised(c, Epi::PLAIN, T, 1, T, static_cast<int>(H));
+        const GemmPlan q2 = bigq ? plan_gemm_fp8_big(Epi::PLAIN, T, 1, static_cast<int>(H))
+                                 : plan_quantised(c, Epi::PLAIN, T, 1, T, static_cast<int>(H));
         StageTimer tm(MOE_STAGE_SHARED_DOWN, s);
         return launch_quantised(c, Epi::PLAIN, s2, q2, s);
     }

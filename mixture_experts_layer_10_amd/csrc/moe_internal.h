@@ -109,6 +109,8 @@ hipError_t launch_gemm_big(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStr
 hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* q, float* scale, int64_t rows, int cols, hipStream_t s);
 GemmPlan plan_gemm_fp8(Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N);
 hipError_t launch_gemm_fp8(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
+// Compute-bound shapes (fp8): 256 x 256 tiles staged through LDS.
+GemmPlan plan_gemm_fp8_big(Epi epi, int64_t rows_upper, int n_groups, int N);
 
 // --- FP4 (MX) weights: activation quantisation and the scaled-MFMA GEMM -----
 hipError_t launch_quant_mx(const void* x_bf16, uint8_t* q, uint8_t* scale, int64_t rows, int cols, hipStream_t s);

@@ -195,6 +195,11 @@ LAYER_CASES = {
     # fp8 64-row tiles on 8 wavefronts (routed, ~57 rows per expert) and
     # 128-row tiles (shared expert, 600 rows)
     "small_fp8_bm64_bm128": lambda: _small(dtype="fp8", T=600, score_bias="zero"),
+    # the shared expert on fp8 256 x 256 LDS tiles (from 1024 rows): ragged
+    # last row tile, and a wider layer (five h column tiles, four output tiles)
+    "small_fp8_shared_big": lambda: _small(dtype="fp8", T=1100, score_bias="zero"),
+    "small_fp8_shared_big_wide": lambda: _small(dtype="fp8", T=1100, hidden=1024, shared_inter=640,
+                                                score_bias="zero"),
     # FP4 (MX) weights: 32-row tiles (~14 rows per expert), 64-row tiles on 8
     # wavefronts (~56 rows per expert; shared expert 600 rows), a local share
     # with a wider layer, capacity drops, one token, and the full-decode shape
@@ -250,7 +255,16 @@ def test_layer_stages_match_oracle(name):
         else:
             assert float(np.max(row_err)) < tol
     if ref["shared"] is not None:
-        assert _rel(host(r["shared"]), ref["shared"]) < tol
+        if w["dtype"] in ("fp8", "mxfp4"):
+            # h requantised on both sides: the rare row with an h code one
+            # step apart, as for the routed rows above
+            s_got, s_want = host(r["shared"]).astype(np.float64), ref["shared"]
+            s_rms = math.sqrt(float(np.mean(s_want * s_want)))
+            s_err = np.max(np.abs(s_got - s_want), axis=1) / s_rms
+            assert float(np.quantile(s_err, 0.99)) < tol
+            assert float(np.max(s_err)) < 4 * tol
+        else:
+            assert _rel(host(r["shared"]), ref["shared"]) < tol
     err = _rel(host(r["y"]), ref["y"])
     say("  max|dy|/rms =", err)
     assert err < tol
