@@ -59,6 +59,8 @@ ROUTE_CASES = [
     dict(n_experts=32, top_k=4, n_group=4, topk_group=2, score_fn="softmax", routed_scale=2.5),
     dict(n_experts=512, top_k=8, n_group=16, topk_group=4, score_fn="sigmoid", bias=True),
     dict(n_experts=96, top_k=3, n_group=32, topk_group=3, score_fn="sigmoid", renormalize=False),
+    # the largest supported router: 512 experts in 64 groups, 16 kept, top-16
+    dict(n_experts=512, top_k=16, n_group=64, topk_group=16, score_fn="sigmoid", bias=True),
 ]
 
 
@@ -128,6 +130,7 @@ DISPATCH_CASES = [
     (1, 256, 8, 0, 256, 0.0, 0.0),
     (777, 64, 4, 60, 64, 1.0, 2.0),          # small share at the end, capacity
     (5000, 512, 4, 0, 512, 0.0, 0.5),        # widest expert count
+    (1000, 512, 16, 0, 512, 1.0, 1.0),       # top-16 of 512, capacity, skew
 ]
 
 
@@ -200,6 +203,12 @@ LAYER_CASES = {
     "small_fp8_shared_big": lambda: _small(dtype="fp8", T=1100, score_bias="zero"),
     "small_fp8_shared_big_wide": lambda: _small(dtype="fp8", T=1100, hidden=1024, shared_inter=640,
                                                 score_bias="zero"),
+    # the largest router (512 experts, 64 groups, top-16) through the layer
+    "small_bf16_max_router": lambda: _small(T=64, n_experts=512, expert_end=512, top_k=16, n_group=64,
+                                            topk_group=16, hidden=256, inter=128, shared_inter=128),
+    # a local share at the end of the expert range that three tokens barely reach
+    "small_bf16_sparse_share": lambda: _small(T=3, expert_begin=60, expert_end=64, top_k=2, n_group=1,
+                                              topk_group=1),
     # FP4 (MX) weights: 32-row tiles (~14 rows per expert), 64-row tiles on 8
     # wavefronts (~56 rows per expert; shared expert 600 rows), a local share
     # with a wider layer, capacity drops, one token, and the full-decode shape
