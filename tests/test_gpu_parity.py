@@ -203,6 +203,11 @@ LAYER_CASES = {
     "small_fp8_shared_big": lambda: _small(dtype="fp8", T=1100, score_bias="zero"),
     "small_fp8_shared_big_wide": lambda: _small(dtype="fp8", T=1100, hidden=1024, shared_inter=640,
                                                 score_bias="zero"),
+    # skewed, capacity-capped fp8 routing with groups from a few rows to 375
+    # (several row tiles each), at the model's intermediate sizes, so that one
+    # e4m3 step of one h element stays within the bound on y
+    "small_fp8_skew_groups": lambda: _small(dtype="fp8", T=2000, inter=2048, shared_inter=2048, capacity_factor=2.0,
+                                             router_bias="zipf1.1", score_bias="zero"),
     # the largest router (512 experts, 64 groups, top-16) through the layer
     "small_bf16_max_router": lambda: _small(T=64, n_experts=512, expert_end=512, top_k=16, n_group=64,
                                             topk_group=16, hidden=256, inter=128, shared_inter=128),
