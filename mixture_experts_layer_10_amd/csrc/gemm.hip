@@ -446,12 +446,9 @@ template <Elem EL, Epi EPI, int BM, int PD, int APD, bool SMAJOR = false, bool A
 void launch_one(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     constexpr size_t lds = 2 * static_cast<size_t>(BM) * Tr<EL>::kRowG * 16;
     if constexpr (lds > 65536) {
-        static bool attr_set = false;          // once per instantiation
-        if (!attr_set) {
-            (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<EL, EPI, BM, PD, APD, SMAJOR, ASPLIT, NW>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-            attr_set = true;
-        }
+        static std::atomic<int> lds_set[kMaxDevices];
+        (void)ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<EL, EPI, BM, PD, APD, SMAJOR, ASPLIT, NW>),
+                                 static_cast<int>(lds), lds_set);
     }
     hipLaunchKernelGGL((gemm_kernel<EL, EPI, BM, PD, APD, SMAJOR, ASPLIT, NW>), dim3(static_cast<unsigned>(p.grid)), dim3(NW * 64),
                        lds, s, a, p.n_tiles);

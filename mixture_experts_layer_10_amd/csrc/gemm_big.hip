@@ -257,13 +257,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
 template <Epi EPI, int NW>
 hipError_t launch_big_epi(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     constexpr int lds = kStages * kStageB;
-    static bool attr_set = false;              // once per instantiation
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<EPI, NW>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<int> lds_set[kMaxDevices];
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_big_kernel<EPI, NW>), lds, lds_set);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemm_big_kernel<EPI, NW>), dim3(static_cast<unsigned>(p.grid)), dim3(NW * 64), lds, s, a,
                        p.n_tiles);
     return hipGetLastError();

@@ -584,13 +584,9 @@ __global__ __launch_bounds__(512, 1) void gemm_big_fp8_kernel(GemmArgs a, int n_
 template <Epi EPI>
 hipError_t launch_big_fp8(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     constexpr int lds = kBigStages * kBigStageB;
-    static bool attr_set = false;              // once per instantiation
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_fp8_kernel<EPI>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<int> lds_set[kMaxDevices];
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_big_fp8_kernel<EPI>), lds, lds_set);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemm_big_fp8_kernel<EPI>), dim3(static_cast<unsigned>(p.grid)), dim3(512), lds, s, a, p.n_tiles);
     return hipGetLastError();
 }

@@ -424,13 +424,9 @@ template <Epi EPI, int BM, int NW, int CK, int PD, int OCC>
 hipError_t launch_mx_one(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     auto* kern = &gemm_mx_kernel<EPI, BM, NW, CK, PD, OCC>;
     const int dyn = mx_scale_lds_bytes(a.K);
-    static int attr = 0;                       // dynamic LDS limit raised so far (per instantiation)
-    if (dyn > attr) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
-        if (e != hipSuccess) return e;
-        attr = dyn;
-    }
+    static std::atomic<int> lds_set[kMaxDevices];
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), dyn, lds_set);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(p.grid)), dim3(NW * 64), static_cast<size_t>(dyn), s, a,
                        p.n_tiles);
     return hipGetLastError();

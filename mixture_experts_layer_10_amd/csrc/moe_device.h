@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -11,6 +13,25 @@ namespace moe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Host side: raises `kernel`'s dynamic-LDS limit to `bytes` on the current
+// device (hipFuncSetAttribute acts on the device current at the call), once
+// per device and size. `done` holds, per device, the largest limit set so
+// far; give each kernel instantiation an array of its own.
+constexpr int kMaxDevices = 64;
+inline hipError_t ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<int>* done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire) >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+        int cur = done[dev].load(std::memory_order_relaxed);
+        while (cur < bytes && !done[dev].compare_exchange_weak(cur, bytes, std::memory_order_release)) {
+        }
+    }
+    return e;
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);

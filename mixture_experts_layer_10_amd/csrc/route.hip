@@ -70,17 +70,33 @@ __device__ __forceinline__ bool better(float v, int i, float w, int j) {
     return v > w || (v == w && i < j);
 }
 
-// Butterfly arg-max over the 64 lanes; every lane ends with the winner.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(v, off, 64);
-        const int oi = __shfl_xor(i, off, 64);
-        if (better(ov, oi, v, i)) {
-            v = ov;
-            i = oi;
-        }
+// One step of the arg-max reduction: take the pair DPP control CTRL brings
+// from another lane if it is better; lanes CTRL gives no source (or rows
+// outside ROW_MASK) compare with their own pair and keep it.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_dpp(float& v, int& i) {
+    const int vb = __builtin_bit_cast(int, v);
+    const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(vb, vb, CTRL, ROW_MASK, 0xf, false));
+    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xf, false);
+    if (better(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
     }
+}
+
+// Arg-max over the 64 lanes with the gfx9 DPP reduction (row_shr 1, 2, 4, 8
+// within each 16-lane row, then row_bcast 15 and 31 across rows) into lane
+// 63, read back as a wave-uniform pair. "better" is a total order on (value,
+// index), so the winner does not depend on the reduction order.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+    argmax_dpp<0x111, 0xf>(v, i);        // row_shr:1
+    argmax_dpp<0x112, 0xf>(v, i);        // row_shr:2
+    argmax_dpp<0x114, 0xf>(v, i);        // row_shr:4
+    argmax_dpp<0x118, 0xf>(v, i);        // row_shr:8  (lane 15 of each row: the row's best)
+    argmax_dpp<0x142, 0xa>(v, i);        // row_bcast:15 into rows 1 and 3
+    argmax_dpp<0x143, 0xc>(v, i);        // row_bcast:31 into rows 2 and 3 (lane 63: the best)
+    v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    i = __builtin_amdgcn_readlane(i, 63);
 }
 
 constexpr int kMaxE = 512;
@@ -125,7 +141,34 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
         const int gs = E / a.G;
         float gscore = -INFINITY;
         int gid = 0x7fffffff;
-        if (lane < a.G) {
+        const int lpg = gs / EPL;                       // lanes per group, when whole
+        if (gs % EPL == 0 && lpg >= 1 && lpg <= 64 && (lpg & (lpg - 1)) == 0 && E == 64 * EPL) {
+            // each lane's two best, then a butterfly over the group's lanes:
+            // the top two of a union of two top-twos (t1 >= t2, o1 >= o2) are
+            // max(t1, o1) and max(min(t1, o1), max(t2, o2))
+            float t1 = -INFINITY, t2 = -INFINITY;
+#pragma unroll
+            for (int q = 0; q < EPL; ++q) {
+                const float v = s_sel[lane * EPL + q];
+                if (v > t1) {
+                    t2 = t1;
+                    t1 = v;
+                } else if (v > t2) {
+                    t2 = v;
+                }
+            }
+            for (int off = 1; off < lpg; off <<= 1) {
+                const float o1 = __shfl_xor(t1, off, 64);
+                const float o2 = __shfl_xor(t2, off, 64);
+                const float n1 = fmaxf(t1, o1);
+                t2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
+                t1 = n1;
+            }
+            if (lane % lpg == 0) {
+                gscore = gs >= 2 ? t1 + t2 : t1;
+                gid = lane / lpg;
+            }
+        } else if (lane < a.G) {
             float t1 = -INFINITY, t2 = -INFINITY;
             for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
                 const float v = s_sel[e];
@@ -145,7 +188,7 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
             int i = gid;
             wave_argmax(v, i);
             keep |= 1ull << i;
-            if (lane == i) {
+            if (gid == i) {                             // the lane that holds group i
                 gscore = -INFINITY;
                 gid = 0x7fffffff;
             }
