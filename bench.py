@@ -41,6 +41,8 @@ def parse():
                     help="capture the timed steps in one HIP graph and replay it (no launch gaps)")
     ap.add_argument("--diag-steps", type=int, default=10,
                     help="untimed steps with events around every stage, for the per-stage breakdown")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak yardsticks (MFMA loop, device copy)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the layer, run a plain device copy of MIB MiB 5 times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -95,6 +97,56 @@ def calibrate_copy(mib):
     dt = (time.perf_counter() - t0) / 5
     print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4,
                       "launches": 6, "copy_gbs_read_plus_write": 2 * n * 4 / dt / 1e9}), flush=True)
+
+
+def achievable_peaks():
+    """Yardsticks measured on this device, beside the spec peaks: the bf16
+    matrix-core rate of a loop of independent MFMAs on every SIMD (no memory
+    traffic) with the shader clock it ran at, the rate at which a plain
+    coalesced read streams 4 GiB in from HBM, and the read + write rate of a
+    device copy of 2 GiB (torch's copy kernel). Medians of 3 timed launches
+    after one untimed one."""
+    import torch
+    from mixture_experts_layer_10_amd import mfma_loop, stream_read
+    out = torch.zeros(3, dtype=torch.int64, device="cuda")
+    mfma_loop(20000, out)
+    rates, clocks = [], []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = mfma_loop(300000, out)
+        e1.record()
+        e1.synchronize()
+        rates.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        ticks, rt = out[:2].tolist()
+        clocks.append(ticks / rt * 100.0)
+    buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream_read(buf, sink)
+    rd = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        nb = stream_read(buf, sink)
+        e1.record()
+        e1.synchronize()
+        rd.append(nb / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    n = (2 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    gbs = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        gbs.append(2 * n * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return {"mfma_loop_bf16_tflops": float(np.median(rates)), "mfma_loop_sclk_mhz": float(np.median(clocks)),
+            "stream_read_gbs": float(np.median(rd)), "copy_gbs": float(np.median(gbs))}
 
 
 def stage_bytes_flops(w, counts, stage):
@@ -238,6 +290,18 @@ def main():
     torch.cuda.synchronize()
     prof = moe.profile_query()
     moe.profile_enable(0)
+
+    # per-step times: a separate pass with an event between steps (kept out
+    # of the timed region, which has no events between steps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    evs[0].record()
+    for i in range(a.steps):
+        step()
+        evs[i + 1].record()
+    evs[-1].synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps)])
+    step_pct = {"median": float(np.median(per_step)), "p10": float(np.percentile(per_step, 10)),
+                "p90": float(np.percentile(per_step, 90)), "source": "separate pass, an event between steps"}
     graphed = graph is not None
     del graph
 
@@ -294,6 +358,17 @@ def main():
                    "ep8_replanned_imbalance": moe.moe_eplb_plan(lc, 8, 0)[3],
                    "ep8_replanned_8_redundant_imbalance": moe.moe_eplb_plan(lc, 8, 8)[3]}
 
+    peaks = None
+    if not a.no_peaks:
+        peaks = achievable_peaks()
+        if roof["unit"] == "GB/s":
+            peaks["dominant_frac_of_achievable"] = roof["achieved"] / peaks["stream_read_gbs"]
+        elif w["dtype"] == "bf16":
+            peaks["dominant_frac_of_achievable"] = roof["achieved"] / peaks["mfma_loop_bf16_tflops"]
+        grouped["hbm_frac_of_stream_read"] = gb / gt / 1e9 / peaks["stream_read_gbs"]
+        if w["dtype"] == "bf16":
+            grouped["mfma_frac_of_loop"] = gf / gt / 1e12 / peaks["mfma_loop_bf16_tflops"]
+
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -304,6 +379,8 @@ def main():
         "roofline": roof,
         "grouped_gemm": grouped,
         "stage_ms": stage_ms,
+        "step_ms": step_pct,
+        "achievable": peaks,
         "rows": int(counts.sum()), "max_rows_per_expert": int(counts.max()),
         "expert_load": expert_load,
     }

@@ -299,6 +299,27 @@ int moe_profile_reset(void);
 int moe_profile_select(unsigned stage_mask);
 int moe_profile_query(int stage, double* total_ms, int* count);
 
+/* ---- Diagnostics: the matrix-core rate the chip sustains -------------------
+ * Not part of the layer; a yardstick for the grouped GEMMs' MFMA fraction.
+ * moe_mfma_loop launches two workgroups of four wavefronts per compute unit;
+ * each wavefront runs `iters` (1 .. 2^40) iterations of four independent
+ * v_mfma_f32_32x32x16_bf16 chains on pseudo-random bf16 operands, and no
+ * memory traffic. *flops (host) receives the FLOPs the launch performs.
+ * out (device uint64 [3], 8-byte aligned) receives, for wavefront 0 of
+ * workgroup 0: the shader-clock ticks and the 100 MHz real-time ticks its
+ * loop took (their ratio times 100 MHz is the shader clock it ran at), and a
+ * checksum of its accumulators. The caller times the launch (stream-ordered
+ * and asynchronous like every call here). */
+int moe_mfma_loop(int64_t iters, uint64_t* out, double* flops, hipStream_t stream);
+
+/* moe_stream_read: reads the `bytes` (a multiple of 16, >= 0) of device
+ * buffer src (16-byte aligned) once, coalesced, eight 16-byte loads in
+ * flight per lane, and writes almost nothing (out, device uint32 [1], is
+ * written only if the XOR of the data equals 0x9e3779b9); timing it gives
+ * the rate at which this device streams weights in from HBM. bytes == 0 is
+ * a no-op. Not part of the layer. */
+int moe_stream_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,5 +10,5 @@ from .binding import (  # noqa: F401
     moe_eplb_plan,
     LIB_PATH,
     SCORE_SOFTMAX, SCORE_SIGMOID, DTYPE_F32, DTYPE_BF16, DTYPE_FP8, DTYPE_MXFP4,
-    STAGES, profile_enable, profile_reset, profile_query, profile_select,
+    STAGES, profile_enable, profile_reset, profile_query, profile_select, mfma_loop, stream_read,
 )

@@ -80,6 +80,9 @@ def lib():
             "moe_profile_select": (ctypes.c_int, [ctypes.c_uint]),
             "moe_profile_query": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                                   ctypes.POINTER(ctypes.c_int)]),
+            "moe_mfma_loop": (ctypes.c_int, [ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
+                                             ctypes.c_void_p]),
+            "moe_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -370,3 +373,28 @@ def profile_query():
         _check(lib().moe_profile_query(i, ctypes.byref(ms), ctypes.byref(n)), "moe_profile_query")
         out[name] = (ms.value, n.value)
     return out
+
+
+def mfma_loop(iters, out, stream=None):
+    """Launch the matrix-core loop (moe_mfma_loop): `out` is a device int64
+    tensor of at least 3 elements that receives the shader-clock ticks, the
+    100 MHz real-time ticks and a checksum; returns the launch's FLOPs."""
+    p = _ptr(out, dtype=torch.int64, name="out")
+    if out.numel() < 3:
+        raise ValueError("out must hold at least 3 elements")
+    flops = ctypes.c_double(0)
+    _check(lib().moe_mfma_loop(int(iters), ctypes.c_void_p(p), ctypes.byref(flops), _stream(stream)),
+           "moe_mfma_loop")
+    return flops.value
+
+
+def stream_read(src, out, stream=None):
+    """Read every byte of device tensor `src` once (moe_stream_read); `out` is a
+    device int32 tensor of at least 1 element. Returns the bytes read."""
+    if not src.is_contiguous() or not src.is_cuda:
+        raise ValueError("src must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    p = _ptr(out, dtype=torch.int32, name="out")
+    _check(lib().moe_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(p), _stream(stream)),
+           "moe_stream_read")
+    return nbytes

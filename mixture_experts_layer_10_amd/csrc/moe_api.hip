@@ -763,4 +763,17 @@ int moe_profile_query(int stage, double* total_ms, int* count) {
     return MOE_OK;
 }
 
+int moe_mfma_loop(int64_t iters, uint64_t* out, double* flops, hipStream_t stream) {
+    if (iters < 1 || iters > (int64_t{1} << 40) || !out || !flops) return MOE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(out) % 8) return MOE_ERR_MISALIGNED;
+    return hip_status(launch_mfma_loop(iters, reinterpret_cast<unsigned long long*>(out), flops, stream));
+}
+
+int moe_stream_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t stream) {
+    if (bytes < 0 || bytes % 16 || (bytes > 0 && !src) || !out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(src) || reinterpret_cast<uintptr_t>(out) % 4) return MOE_ERR_MISALIGNED;
+    if (bytes == 0) return MOE_OK;
+    return hip_status(launch_stream_read(src, bytes, out, stream));
+}
+
 }  // extern "C"

@@ -119,6 +119,8 @@ hipError_t launch_gemm_mx(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStre
 
 // --- expert load statistics and placement -----------------------------------
 hipError_t launch_expert_load(const int32_t* ids, int64_t n, int E, int64_t* load, hipStream_t s);
+hipError_t launch_mfma_loop(int64_t iters, unsigned long long* out, double* flops, hipStream_t s);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t s);
 void plan_placement(const int64_t* load, int E, int ranks, int redundant, int32_t* replicas, int32_t* slot_expert,
                     double* rank_load);
 

@@ -128,6 +128,18 @@ def test_stage_calls_reject_before_launch():
     assert L.moe_quantize_mx(cp, 4, FAKE, FAKE, FAKE, None) == B.ERR_INVALID_ARG
     assert L.moe_quantize_mx(mxp, 4, FAKE + 8, FAKE, FAKE, None) == B.ERR_MISALIGNED
     assert L.moe_quantize_mx(mxp, 0, None, None, None, None) == B.OK
+    # the MFMA-loop yardstick: iteration count, output pointer and alignment
+    fl = ctypes.c_double(0)
+    assert L.moe_mfma_loop(0, FAKE, ctypes.byref(fl), None) == B.ERR_INVALID_ARG
+    assert L.moe_mfma_loop(1 << 41, FAKE, ctypes.byref(fl), None) == B.ERR_INVALID_ARG
+    assert L.moe_mfma_loop(10, None, ctypes.byref(fl), None) == B.ERR_INVALID_ARG
+    assert L.moe_mfma_loop(10, FAKE, None, None) == B.ERR_INVALID_ARG
+    assert L.moe_mfma_loop(10, FAKE + 4, ctypes.byref(fl), None) == B.ERR_MISALIGNED
+    assert L.moe_stream_read(FAKE, 24, FAKE, None) == B.ERR_INVALID_ARG        # not a multiple of 16
+    assert L.moe_stream_read(None, 32, FAKE, None) == B.ERR_INVALID_ARG
+    assert L.moe_stream_read(FAKE, 32, None, None) == B.ERR_INVALID_ARG
+    assert L.moe_stream_read(FAKE + 8, 32, FAKE, None) == B.ERR_MISALIGNED
+    assert L.moe_stream_read(None, 0, FAKE, None) == B.OK
     # invalid config is reported by every entry point
     bad = _good(n_group=7)
     assert L.moe_forward(ctypes.byref(bad), 4, FAKE, FAKE, None, None, ctypes.byref(W), FAKE, None, None,
