@@ -10,8 +10,8 @@
 //
 //  * a workgroup computes 256 rows x 256 weight rows; its NW wavefronts
 //    (8 by default, two per SIMD; 4 also built) form 2 x NW/2 and each
-//    computes 128 rows x 512/NW weight rows as 32 x 32 fragments of
-//    v_mfma_f32_32x32x16_bf16;
+//    computes four 32-row blocks x 512/NW weight rows as 32 x 32 fragments
+//    of v_mfma_f32_32x32x16_bf16;
 //  * both operands go HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR
 //    staging), K = 64 per stage: each row's 128 bytes are one whole cache
 //    line, so a load instruction touches 8 lines (half-line loads, 16 rows of
@@ -27,7 +27,9 @@
 //  * SwiGLU tiles interleave gate and up rows so that each wavefront holds
 //    matching gate and up columns: h = silu(g) * u is formed in registers;
 //  * a group's rows are split evenly over its m-tiles, and 32-row blocks past
-//    a tile's real row count skip their MFMAs.
+//    a tile's real row count skip their MFMAs; in such a short tile the two
+//    wavefront rows take alternate blocks, so its busier row does
+//    ceil(blocks / 2) blocks of work rather than min(blocks, 4).
 #include <utility>
 
 #include "gemm_tile.h"
@@ -64,8 +66,8 @@ __device__ __forceinline__ float silu_mul_big(float g, float u) {
 // [6:4], lgkmcnt [11:8]).
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-// NW wavefronts as 2 (rows) x NW/2 (columns); each computes 128 rows x
-// WB = 512 / NW weight rows. With NW = 8 two wavefronts share each SIMD, so
+// NW wavefronts as 2 (rows) x NW/2 (columns); each computes four 32-row
+// blocks x WB = 512 / NW weight rows. With NW = 8 two wavefronts share each SIMD, so
 // one issues MFMAs while the other waits at a barrier or on LDS.
 template <Epi EPI, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_tiles) {
@@ -142,7 +144,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
     int f_off[KSTEPS];
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) f_off[t] = fr * kRowB + (((2 * t + (lane >> 5)) ^ swz(fr)) * 16);
-    const int a_base = wm * 128 * kRowB;
     const int b_base = kBM * kRowB + wn * WB * kRowB;
     const int nrb = (rows + 31) >> 5;                               // 32-row blocks with data
 
@@ -152,14 +153,25 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
-    // Rows blocks of this wavefront that hold data (uniform: scalar branches).
-    const int nbw = min(max(nrb - wm * 4, 0), 4);
+    // Block i of wavefront row wm is the tile's 32-row block b0 + i * bs. A
+    // full tile gives each row four consecutive blocks; a tile cut short by
+    // its group's row count alternates them (row wm takes blocks wm, wm + 2,
+    // wm + 4, wm + 6), so both rows keep about equal work: the MFMAs of a
+    // block with no rows are skipped, and a tile lasts as long as its busier
+    // row. nbw = blocks of this wavefront that hold data (uniform: scalar
+    // branches).
+    const bool full = nrb == 8;
+    const int b0 = full ? wm * 4 : wm, bs = full ? 1 : 2;
+    const int nbw = full ? 4 : min(max((nrb - wm + 1) >> 1, 0), 4);
+    int a_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_off[i] = (b0 + i * bs) * 32 * kRowB;
     // Fragments of k-steps 0..3 of a stage (4 x (4 A + NJ B) registers).
     bf16x8 af[KSTEPS][4], bfr[KSTEPS][NJ];
     auto read = [&](int slot, int t) __attribute__((always_inline)) {
         const unsigned char* st = s_ring + slot * kStageB;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[t][i] = lds_frag(st + a_base + i * 32 * kRowB + f_off[t]);
+        for (int i = 0; i < 4; ++i) af[t][i] = lds_frag(st + a_off[i] + f_off[t]);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) bfr[t][j] = lds_frag(st + b_base + j * 32 * kRowB + f_off[t]);
     };
@@ -222,10 +234,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
     const int lc = lane & 31, lh = lane >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (wm * 4 + i < nrb) {
+        if (b0 + i * bs < nrb) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int r = wm * 128 + i * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+                const int r = (b0 + i * bs) * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
                 if (r < rows) {
                     const int64_t rb = (crow0 + r) * a.ldc;
                     if constexpr (EPI == Epi::SWIGLU) {
