@@ -12,7 +12,7 @@
 // taken in token order.
 //
 // Three launches, no atomics whose order reaches a result:
-//   1. per-chunk LDS histograms (a chunk is kDispatchChunk consecutive pairs);
+//   1. per-chunk LDS histograms (a chunk is dispatch_chunk(P) consecutive pairs);
 //   2. one workgroup scans the histograms column-wise (per expert, over
 //      chunks) and across experts -> raw counts, counts, offsets;
 //   3. per chunk, stable in-chunk ranks from wavefront ballots, then
@@ -23,6 +23,12 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+// Histograms up to this size are scanned from LDS. Kept small (with the
+// 5 KB of static arrays, 17 KB) so that the one-workgroup scan fits on a CU
+// beside a 256 x 256 GEMM workgroup of the shared expert (128-133 KB of the
+// 160 KB), which may be running on a second stream; a larger request waits
+// for such a workgroup to finish.
+constexpr size_t kScanStageBytes = 12 * 1024;
 
 __device__ __forceinline__ int local_expert(int id, int E, int begin, int El) {
     if (id < 0 || id >= E) return El;        // invalid id: treated as non-local
@@ -35,8 +41,9 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(DispatchArgs a) {
     const int El = a.El;
     for (int i = threadIdx.x; i < El; i += kThreads) s_hist[i] = 0;
     __syncthreads();
-    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
-    const int64_t p1 = min(p0 + kDispatchChunk, a.P);
+    const int64_t cl = dispatch_chunk(a.P);
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * cl;
+    const int64_t p1 = min(p0 + cl, a.P);
     for (int64_t p = p0 + threadIdx.x; p < p1; p += kThreads) {
         const int le = local_expert(a.ids[p], a.E, a.begin, El);
         if (le < El) atomicAdd(&s_hist[le], 1);
@@ -46,17 +53,54 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(DispatchArgs a) {
     for (int i = threadIdx.x; i < El; i += kThreads) out[i] = s_hist[i];
 }
 
+// Per expert, the running sum of its chunk histograms down the chunks (->
+// chunk bases, raw count), then the capped counts and their exclusive scan
+// across experts (-> offsets). With STAGED the histograms are first copied
+// into LDS by coalesced loads, so the column walks read LDS instead of
+// waiting on one global load per chunk.
+template <bool STAGED>
 __global__ __launch_bounds__(kThreads) void scan_kernel(DispatchArgs a, int nchunk) {
     __shared__ int s_off[4 * kThreads];
     __shared__ int s_part[kThreads];
+    extern __shared__ int s_hist[];                    // [nchunk * El] when STAGED
     const int El = a.El;
+    const int64_t n = static_cast<int64_t>(nchunk) * El;
+    if constexpr (STAGED) {
+        // sixteen independent loads in flight per thread, then their stores
+        constexpr int kBatch = 16;
+        for (int64_t b = threadIdx.x; b < n; b += kBatch * kThreads) {
+            int v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int64_t i = b + j * kThreads;
+                v[j] = i < n ? a.chunk_hist[i] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int64_t i = b + j * kThreads;
+                if (i < n) s_hist[i] = v[j];
+            }
+        }
+        __syncthreads();
+    }
     for (int e = threadIdx.x; e < El; e += kThreads) {
+        // down the column in batches of eight chunks: the batch's reads are
+        // independent, so only one read latency per batch is exposed
         int run = 0;
-        for (int c = 0; c < nchunk; ++c) {
-            const int64_t i = static_cast<int64_t>(c) * El + e;
-            const int h = a.chunk_hist[i];
-            a.chunk_base[i] = run;
-            run += h;
+        for (int c0 = 0; c0 < nchunk; c0 += 8) {
+            int h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t i = static_cast<int64_t>(c0 + j) * El + e;
+                h[j] = c0 + j < nchunk ? (STAGED ? s_hist[i] : a.chunk_hist[i]) : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (c0 + j < nchunk) {
+                    a.chunk_base[static_cast<int64_t>(c0 + j) * El + e] = run;
+                    run += h[j];
+                }
+            }
         }
         if (a.raw) a.raw[e] = run;
         const int cnt = static_cast<int64_t>(run) < a.cap ? run : static_cast<int>(a.cap);
@@ -91,8 +135,9 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DispatchArgs a) {
     int nbits = 1;
     while ((1 << nbits) <= El) ++nbits;    // enough bits for 0..El
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int64_t p0 = chunk * kDispatchChunk;
-    const int64_t p1 = min(p0 + kDispatchChunk, a.P);
+    const int64_t cl = dispatch_chunk(a.P);
+    const int64_t p0 = chunk * cl;
+    const int64_t p1 = min(p0 + cl, a.P);
     for (int64_t base = p0; base < p1; base += kThreads) {
         const int64_t p = base + threadIdx.x;
         const bool valid = p < p1;
@@ -141,7 +186,11 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     if (nchunk == 0) return hipSuccess;
     hipLaunchKernelGGL(hist_kernel, dim3(static_cast<unsigned>(nchunk)), dim3(kThreads),
                        sizeof(int) * a.El, s, a);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kThreads), 0, s, a, static_cast<int>(nchunk));
+    const size_t hist_bytes = sizeof(int) * static_cast<size_t>(nchunk) * a.El;
+    if (hist_bytes <= kScanStageBytes)
+        hipLaunchKernelGGL(scan_kernel<true>, dim3(1), dim3(kThreads), hist_bytes, s, a, static_cast<int>(nchunk));
+    else
+        hipLaunchKernelGGL(scan_kernel<false>, dim3(1), dim3(kThreads), 0, s, a, static_cast<int>(nchunk));
     const size_t lds = sizeof(int) * (2 * a.El + 4 * (a.El + 1));
     hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>(nchunk)), dim3(kThreads), lds, s, a);
     return hipGetLastError();

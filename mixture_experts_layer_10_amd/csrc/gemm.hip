@@ -563,6 +563,20 @@ GemmPlan plan_dense_splitk(int64_t T, int N, int K, int chunk) {
     return p;
 }
 
+int64_t splitk_partial_rows_upto(int64_t T, int N, int K, int chunk) {
+    // ksplit * rows grows with T between the row-count breakpoints of
+    // plan_dense_splitk and can drop just past one, so take the largest of T
+    // and each breakpoint below it
+    auto rows = [&](int64_t t) -> int64_t {
+        const GemmPlan p = plan_dense_splitk(t, N, K, chunk);
+        return p.ksplit > 1 ? p.ksplit * t : 0;
+    };
+    int64_t m = rows(T);
+    for (const int64_t t : {int64_t{1024}, int64_t{4096}, int64_t{8192}})
+        if (t < T) m = std::max(m, rows(t));
+    return m;
+}
+
 hipError_t launch_splitk_reduce(const GemmArgs& a, int ksplit, hipStream_t s) {
     if (ksplit <= 1) return hipSuccess;
     const int64_t n4 = (static_cast<int64_t>(a.T) * a.ldc + 3) / 4;

@@ -77,7 +77,9 @@ int router_chunk(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 64 : 
 Layout layout(const moe_config* c, int64_t T) {
     const int64_t E = c->n_experts, El = c->expert_end - c->expert_begin, k = c->top_k;
     const int64_t P = T * k;
-    const int64_t nchunk = dispatch_chunks(P);
+    // scratch whose need can fall as T grows is sized for the largest need
+    // of any batch up to T, so a workspace sized for T serves them all
+    const int64_t nchunk = dispatch_chunks_upto(P);
     Layout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -96,8 +98,7 @@ Layout layout(const moe_config* c, int64_t T) {
     L.chunk_hist = take(sizeof(int32_t) * nchunk * El);
     L.chunk_base = take(sizeof(int32_t) * nchunk * El);
     L.sched = take(sizeof(int32_t) * (El + 2));
-    const GemmPlan rp = plan_dense_splitk(T, c->n_experts, c->hidden, router_chunk(c));
-    L.partial = take(rp.ksplit > 1 ? sizeof(float) * rp.ksplit * T * E : 0);
+    L.partial = take(sizeof(float) * splitk_partial_rows_upto(T, c->n_experts, c->hidden, router_chunk(c)) * E);
     L.h = take(static_cast<size_t>(act_bytes(c)) * P * c->inter);
     L.h_shared = take(static_cast<size_t>(act_bytes(c)) * T * c->shared_inter);
     L.rows = take(static_cast<size_t>(row_bytes(c)) * P * c->hidden);

@@ -25,7 +25,6 @@ struct RouteArgs {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
 // --- dispatch (K3) -----------------------------------------------------------
-constexpr int kDispatchChunk = 2048;     // pairs per block
 struct DispatchArgs {
     const int32_t* ids;       // [P]
     int32_t* raw;             // [El] or null
@@ -40,7 +39,18 @@ struct DispatchArgs {
     int64_t cap;              // capacity, or INT64_MAX
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
-inline int64_t dispatch_chunks(int64_t P) { return (P + kDispatchChunk - 1) / kDispatchChunk; }
+// Pairs per histogram/scatter block: small batches take short blocks, so that
+// more workgroups share the work and each makes fewer passes; large batches
+// long ones, so that the per-block histograms stay few. A function of P
+// only, so the workspace layout and the kernels agree.
+__host__ __device__ inline int64_t dispatch_chunk(int64_t P) { return P <= 16384 ? 512 : 2048; }
+inline int64_t dispatch_chunks(int64_t P) { return (P + dispatch_chunk(P) - 1) / dispatch_chunk(P); }
+// The most blocks any batch of at most P pairs uses (the short blocks end at
+// 16384 pairs), so that a workspace sized for P serves every smaller batch.
+inline int64_t dispatch_chunks_upto(int64_t P) {
+    const int64_t a = dispatch_chunks(P), b = dispatch_chunks(P < 16384 ? P : 16384);
+    return a > b ? a : b;
+}
 
 // --- grouped GEMM (K1, K5, K6) ----------------------------------------------
 enum class Epi : int { SWIGLU = 0, PLAIN = 1 };
@@ -98,10 +108,12 @@ hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_
 hipError_t launch_gemm(Elem e, Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
 // Dense (single-group) PLAIN GEMM with fp32 output, split along K when the
 // tile grid alone would leave the GPU idle; `partial` must hold
-// max_split * T * N floats.
+// ksplit * T * N floats. splitk_partial_rows_upto(T, ...) * N floats cover
+// every batch of at most T rows.
 GemmPlan plan_dense_splitk(int64_t T, int N, int K, int chunk);
+int64_t splitk_partial_rows_upto(int64_t T, int N, int K, int chunk);
 hipError_t launch_splitk_reduce(const GemmArgs& a, int ksplit, hipStream_t s);
-// Compute-bound shapes (bf16): 256 x 256 tiles through a 4-stage LDS ring.
+// Compute-bound shapes (bf16): 256 x 256 tiles through a 2-stage LDS ring.
 GemmPlan plan_gemm_big(Epi epi, int64_t rows_upper, int n_groups, int N);
 hipError_t launch_gemm_big(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
 

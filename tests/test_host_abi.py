@@ -82,6 +82,23 @@ def test_workspace_bytes_grows_with_tokens():
     assert moe.lib().moe_workspace_bytes(ctypes.byref(c), -1, ctypes.byref(n)) == B.ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(dtype="fp8", expert_end=256), dict(dtype="mxfp4", top_k=2, topk_group=4),
+                                dict(hidden=512, n_experts=8, top_k=2, inter=512, expert_end=8, n_group=1,
+                                     topk_group=1, score_fn="softmax", shared_inter=0, dtype="f32")],
+                         ids=["ep8_bf16", "full_fp8", "mxfp4_k2", "toy_f32"])
+def test_workspace_bytes_never_shrinks_as_tokens_grow(kw):
+    """A workspace sized for max_tokens must serve every smaller batch: the
+    reported size is non-decreasing in T, across the points where the router
+    GEMM's K split and the dispatch block length change."""
+    c = _good(**kw)
+    k = c.top_k
+    edges = [1024, 4096, 8192, 16384 // k, 16384 // k + 1]
+    Ts = sorted(set(list(range(0, 20000, 97)) + [t + d for t in edges for d in (-1, 0, 1)]))
+    sizes = [moe.workspace_bytes(c, T) for T in Ts]
+    for (t0, a), (t1, b) in zip(zip(Ts, sizes), zip(Ts[1:], sizes[1:])):
+        assert b >= a, (t0, a, t1, b)
+
+
 FAKE = 0x10000  # a 16-byte-aligned address never dereferenced: every call below fails validation first
 
 
