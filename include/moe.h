@@ -313,8 +313,9 @@ int moe_profile_query(int stage, double* total_ms, int* count);
 int moe_mfma_loop(int64_t iters, uint64_t* out, double* flops, hipStream_t stream);
 
 /* moe_stream_read: reads the `bytes` (a multiple of 16, >= 0) of device
- * buffer src (16-byte aligned) once, coalesced, eight 16-byte loads in
- * flight per lane, and writes almost nothing (out, device uint32 [1], is
+ * buffer src (16-byte aligned) once, one workgroup per compute unit, each
+ * taking 64 KB blocks of consecutive memory (sixteen 16-byte loads in flight
+ * per lane), and writes almost nothing (out, device uint32 [1], is
  * written only if the XOR of the data equals 0x9e3779b9); timing it gives
  * the rate at which this device streams weights in from HBM. bytes == 0 is
  * a no-op. Not part of the layer. */
