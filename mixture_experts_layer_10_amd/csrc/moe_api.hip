@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <unordered_map>
 #include <vector>
@@ -332,6 +333,35 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
     return launch_gemm(el, Epi::PLAIN, g2, p2, s);
 }
 
+bool overlap_shared(const moe_config* c, int64_t T);
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+    constexpr int kDevices = 64;
+    static std::atomic<int> cache[kDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+bool shared_big_tiles(const moe_config* c, int64_t T);
+
+// A bf16 shared expert below 1024 tokens that runs beside the routed
+// experts' decode tiles takes the 128 x 128 tiles of gemm_cores.hip, which fit
+// on a CU next to a routed workgroup (measured at the full-decode shape, 512
+// tokens: 4.03 -> 3.96 ms per layer). From 1024 tokens the 256 x 256 tiles
+// stay faster (at the EP8 decode share, 2048 tokens: 0.88 against 0.92 ms),
+// since the shared expert's own operand traffic then competes with the
+// routed weight stream for the CUs' memory path.
+bool shared_cores(const moe_config* c, int64_t T) {
+    return c->dtype == MOE_DTYPE_BF16 && !shared_big_tiles(c, T) && overlap_shared(c, T);
+}
+
 // The shared expert is one dense group of T rows: from 1024 rows on it is
 // compute-bound, and the 256 x 256 LDS-pipelined tiles (bf16, fp8) run it
 // faster than the bandwidth-oriented tiles (bf16: 1.4x at T = 2048).
@@ -385,6 +415,25 @@ hipError_t do_shared_ffn(const moe_config* c, int64_t T, const void* x, const mo
                                  : plan_quantised(c, Epi::PLAIN, T, 1, T, static_cast<int>(H));
         StageTimer tm(MOE_STAGE_SHARED_DOWN, s);
         return launch_quantised(c, Epi::PLAIN, s2, q2, s);
+    }
+    if (shared_cores(c, T)) {
+        const GemmPlan q1 = plan_gemm_cores(Epi::SWIGLU, T, static_cast<int>(Is), device_cus());
+        {
+            StageTimer tm(MOE_STAGE_SHARED_GATE_UP, s);
+            if ((e = launch_gemm_cores(Epi::SWIGLU, s1, q1, s)) != hipSuccess) return e;
+        }
+        GemmArgs s2 = s1;
+        s2.A = s2.A_shared = at<void>(ws, L.h_shared);
+        s2.B = s2.B_shared = wt->shared_w2;
+        s2.K = static_cast<int>(Is);
+        s2.N = static_cast<int>(H);
+        s2.inter = 0;
+        s2.C = s2.C_shared = shared_out;
+        s2.ldc = static_cast<int>(H);
+        s2.out_f32 = 1;
+        const GemmPlan q2 = plan_gemm_cores(Epi::PLAIN, T, static_cast<int>(H), device_cus());
+        StageTimer tm(MOE_STAGE_SHARED_DOWN, s);
+        return launch_gemm_cores(Epi::PLAIN, s2, q2, s);
     }
     const bool big = shared_big_tiles(c, T);
     const GemmPlan q1 = big ? plan_gemm_big(Epi::SWIGLU, T, 1, static_cast<int>(Is))

@@ -116,6 +116,11 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int ksplit, hipStream_t s);
 // Compute-bound shapes (bf16): 256 x 256 tiles through a 2-stage LDS ring.
 GemmPlan plan_gemm_big(Epi epi, int64_t rows_upper, int n_groups, int N);
 hipError_t launch_gemm_big(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
+// The shared expert (one group of T rows, bf16) on 128 x 128 tiles that fit
+// beside the routed decode tiles on a CU (gemm_cores.hip); one persistent
+// workgroup per CU (`cus` = compute units of the device).
+GemmPlan plan_gemm_cores(Epi epi, int64_t T, int N, int cus);
+hipError_t launch_gemm_cores(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
 
 // --- FP8: activation quantisation (K4) and block-scaled grouped GEMM ---------
 hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* q, float* scale, int64_t rows, int cols, hipStream_t s);
