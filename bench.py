@@ -50,7 +50,7 @@ def parse():
 
 
 # Kernel sources whose code a stored traffic measurement belongs to.
-KERNEL_SOURCES = {"bf16": ["gemm.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
+KERNEL_SOURCES = {"bf16": ["gemm.hip", "gemm_big.hip", "gemm_cores.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
                   "f32": ["gemm.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
                   "fp8": ["gemm_fp8.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
                   "mxfp4": ["gemm_mx.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"]}
