@@ -229,12 +229,21 @@ LAYER_CASES = {
 
 
 def _rel(a, b):
+    # a layer whose local share receives no kept pair and that has no shared
+    # expert outputs exact zeros: then the output must be exactly zero too
+    if not np.any(np.asarray(b)):
+        return float(np.max(np.abs(np.asarray(a, dtype=np.float64)))) if np.size(a) else 0.0
     return O.rel_max_err(a, b)
 
 
 @pytest.mark.parametrize("name", list(LAYER_CASES))
 def test_layer_stages_match_oracle(name):
-    w = LAYER_CASES[name]()
+    check_layer(LAYER_CASES[name](), name)
+
+
+def check_layer(w, name):
+    """Every stage of one layer on the GPU against the oracle (shared by the
+    fixed cases here and the random sweep)."""
     say("layer case", name, {k: w[k] for k in ("T", "hidden", "n_experts", "expert_begin", "expert_end", "dtype")})
     big = w["hidden"] >= 4096
     run = Run(w, gen_device="cuda" if big else "cpu")

@@ -3,7 +3,11 @@ bit for bit: 40 router configurations (expert counts 8..512, group structures,
 k up to 16, both score functions, renormalisation, scaling factor, bias, with
 adversarial logits) and 30 dispatch configurations (local shares, capacity,
 skew, batches on both sides of the dispatch block-length switch at 16384
-pairs). Every drawn configuration satisfies the library's validation rules.
+pairs), bit for bit; and 16 random small layers (bf16 and fp32: expert
+counts, groups, k, hidden and intermediate sizes, local shares, capacity,
+score functions, biases, T up to 700, with and without a shared expert), every
+stage against the oracle to the tolerances of the fixed layer cases. Every
+drawn configuration satisfies the library's validation rules.
 """
 import numpy as np
 import pytest
@@ -110,3 +114,38 @@ def test_dispatch_random_configs_bit_exact(i, c):
         assert np.array_equal(got[key], ref[key]), key
     assert np.array_equal(got["perm"][:R], ref["perm"])
     assert np.all(got["perm"][R:] == -7)
+
+
+def _layer_cfgs(n, seed=31):
+    """Random small layers, bf16 and fp32 (the e4m3 / FP4 paths have their
+    own cases at the model's intermediate sizes, where requantisation flips
+    stay rare)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        dtype = str(rng.choice(["bf16", "bf16", "bf16", "f32"]))
+        E = int(rng.choice([8, 16, 32, 64, 128]))
+        groups = [g for g in (1, 2, 4, 8) if E % g == 0 and (g == 1 or E // g >= 2)]
+        G = int(rng.choice(groups))
+        Gk = int(rng.integers(1, G + 1))
+        k = int(rng.integers(1, min(8, Gk * (E // G)) + 1))
+        H = int(rng.choice([128, 256, 512] if dtype == "f32" else [256, 512, 1024]))
+        I = int(rng.choice([128, 256, 384, 640]))
+        b = int(rng.integers(0, E // 2))
+        e = int(rng.integers(b + 1, E + 1))
+        fn = str(rng.choice(["softmax", "sigmoid"]))
+        T = int(rng.integers(1, 300 if dtype == "f32" else 700))
+        out.append(dict(name=f"sweep{len(out)}", T=T, hidden=H, n_experts=E, expert_begin=b, expert_end=e, top_k=k,
+                        n_group=G, topk_group=Gk, score_fn=fn, renormalize=bool(rng.integers(0, 2)),
+                        routed_scale=float(rng.choice([1.0, 2.5])), inter=I,
+                        shared_inter=int(rng.choice([0, 128, 256, 384])), dtype=dtype,
+                        capacity_factor=float(rng.choice([0.0, 0.0, 1.0, 1.5])),
+                        score_bias=("normal0.1" if fn == "sigmoid" and rng.integers(0, 2) else "none"),
+                        router_bias=str(rng.choice(["none", "zipf1.1"]))))
+    return out
+
+
+@pytest.mark.parametrize("w", _layer_cfgs(16), ids=lambda w: w["name"])
+def test_layer_random_configs(w):
+    from test_gpu_parity import check_layer
+    check_layer(w, w["name"])
