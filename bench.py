@@ -183,12 +183,6 @@ def cpu_baseline(w, inp, sample, min_seconds=10.0):
     import torch
     from oracle import moe_oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = None
-
     def h(t):
         if t is None:
             return None
@@ -213,10 +207,25 @@ def cpu_baseline(w, inp, sample, min_seconds=10.0):
         if dt >= min_seconds:
             break
     cores = len(os.sched_getaffinity(0))
+    # the BLAS libraries the oracle's matmuls loaded, and their thread pools
+    # (queried after the passes, once the libraries are loaded)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": d.get("internal_api"), "version": d.get("version"), "threads": d.get("num_threads")}
+                for d in threadpool_info() if d.get("user_api") == "blas"]
+    except Exception:
+        blas = []
+    blas_threads = max([b["threads"] or 1 for b in blas] or [0])
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": passes * S / dt, "unit": "tokens/s", "cores": blas_threads or cores, "kind": "oracle",
             "sample": f"first {S} of {w['T']} tokens of the same workload, whole layer (router GEMM, top-k, "
                       f"dispatch, experts, shared expert, combine), {passes} passes in {dt:.1f} s wall",
-            "affinity_cores": cores, "cpu": platform.processor() or platform.machine()}
+            "affinity_cores": cores, "cpu": cpu, "blas": blas}
 
 
 def main():
