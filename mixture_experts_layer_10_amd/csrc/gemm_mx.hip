@@ -198,16 +198,34 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n
     // (SWIGLU) nt*128 + j (gate) or inter + nt*128 + j - 128 (up), or
     // (PLAIN) nt*256 + j clamped to N - 1; 8 bytes per load, consecutive
     // threads on consecutive bytes of a row. Called once, after the first
-    // chunk's loads are issued and before the first barrier.
+    // chunk's loads are issued and before the first barrier. Loads go out in
+    // batches of kScaleBatch before their stores (a load past the end reads
+    // the last element again and is not stored), so a thread waits once per
+    // batch instead of once per load.
     auto stage_scales = [&]() __attribute__((always_inline)) {
+        constexpr int kScaleBatch = 7;
         const int vpr = kb / 8;
-        for (int v = tid; v < 256 * vpr; v += NT) {
+        const int total = 256 * vpr;
+        auto src = [&](int v) -> uint32_t {
+            v = v < total ? v : total - 1;
             const int j = v / vpr, q = v - j * vpr;
             int wrow;
             if constexpr (EPI == Epi::SWIGLU) wrow = j < 128 ? nt * 128 + j : a.inter + nt * 128 + (j - 128);
             else wrow = min(nt * 256 + j, a.N - 1);
-            const uint2 val = *reinterpret_cast<const uint2*>(Sg + (static_cast<uint32_t>(wrow) * kb + q * 8));
-            *reinterpret_cast<uint2*>(s_bs + j * kbp + q * 8) = val;
+            return static_cast<uint32_t>(wrow) * kb + q * 8;
+        };
+        for (int v0 = tid; v0 < total; v0 += kScaleBatch * NT) {
+            uint2 val[kScaleBatch];
+#pragma unroll
+            for (int s = 0; s < kScaleBatch; ++s) val[s] = *reinterpret_cast<const uint2*>(Sg + src(v0 + s * NT));
+#pragma unroll
+            for (int s = 0; s < kScaleBatch; ++s) {
+                const int v = v0 + s * NT;
+                if (v < total) {
+                    const int j = v / vpr, q = v - j * vpr;
+                    *reinterpret_cast<uint2*>(s_bs + j * kbp + q * 8) = val[s];
+                }
+            }
         }
     };
 
