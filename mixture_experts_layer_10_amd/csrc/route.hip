@@ -116,13 +116,23 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
 
     float sel[EPL];
     int idx[EPL];
+    // all of this lane's logits (and biases) are loaded before any is used,
+    // so the loads are in flight together (indices past E read the last
+    // expert again; those values are not used)
+    float lv[EPL], bv[EPL];
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) lv[q] = lrow[min(lane * EPL + q, E - 1)];
+    if (a.score_bias) {
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) bv[q] = a.score_bias[min(lane * EPL + q, E - 1)];
+    }
 #pragma unroll
     for (int q = 0; q < EPL; ++q) {
         const int e = lane * EPL + q;
         if (e < E) {
-            const float l = lrow[e];
+            const float l = lv[q];
             const float sc = a.score_fn == MOE_SCORE_SIGMOID ? sigmoid_fixed(l) : l;
-            const float v = a.score_bias ? sc + a.score_bias[e] : sc;
+            const float v = a.score_bias ? sc + bv[q] : sc;
             s_logit[e] = l;
             s_score[e] = sc;
             s_sel[e] = v;
