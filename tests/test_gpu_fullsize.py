@@ -1,5 +1,6 @@
 """Parity at the full workload sizes, in the launch configuration the
-benchmark times (moe_forward, bf16 output).
+benchmark times (moe_forward, bf16 output), and at 32 times the EP8 decode
+batch.
 
 At these sizes the oracle cannot run the whole layer in seconds, so:
   * routing ids and gates of EVERY token are compared bit for bit with the
@@ -22,12 +23,17 @@ from gpu_helpers import TOL, host, say
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["ep8_decode_bf16", "full_decode_bf16", "full_prefill_bf16", "fp8_skew", "full_decode_mxfp4"]
+FULL = ["ep8_decode_bf16", "full_decode_bf16", "full_prefill_bf16", "fp8_skew", "full_decode_mxfp4",
+        # the largest batch tested: 65536 tokens at the EP8 share (524288
+        # (token, slot) pairs; about 2048 rows per local expert, so the routed
+        # experts take the 256 x 256 tiles and the shared expert runs after them)
+        ("ep8_decode_bf16", 65536)]
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", FULL, ids=lambda n: n if isinstance(n, str) else f"{n[0]}_T{n[1]}")
 def test_full_size_forward(name):
-    w = workload(name)
+    w = workload(name) if isinstance(name, str) else workload(name[0], T=name[1])
+    name = name if isinstance(name, str) else f"{name[0]}_T{name[1]}"
     T, k, E, H = w["T"], w["top_k"], w["n_experts"], w["hidden"]
     say("full-size case", name, "T", T)
     cfg = moe.config_from_workload(w, out_dtype="bf16")
