@@ -238,38 +238,73 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
     const int64_t crow0 = shared ? m0 : static_cast<int64_t>(row0) + m0;
     unsigned char* Cb = static_cast<unsigned char*>(shared ? a.C_shared : a.C);
     const int lc = lane & 31, lh = lane >> 5;
+    // Outputs are staged in the (now idle) LDS ring as a row-major tile, then
+    // written as whole 16-byte pieces of rows: a lane's own fragment values
+    // are one column each, and storing them directly takes 2- or 4-byte
+    // stores scattered over 16 rows per instruction (measured at the prefill
+    // shape: the down GEMM's stores then cost about 13% of its time). A pass
+    // covers the whole tile for bf16 outputs (at most 128 KB) and half of its
+    // columns for fp32 outputs (two passes of 128 KB each).
+    constexpr int TC = EPI == Epi::SWIGLU ? 128 : kBN;              // output columns of the tile
+    auto epilogue = [&](auto f32_out) __attribute__((always_inline)) {
+        constexpr bool F32 = decltype(f32_out)::value;
+        constexpr int EB = F32 ? 4 : 2;                             // output bytes per element
+        constexpr int PC = F32 ? TC / 2 : TC;                       // columns per pass
+        constexpr int PRB = PC * EB;                                // LDS bytes per tile row in a pass
+        constexpr int GPR = PRB / 16;                               // 16-byte pieces per row in a pass
+        auto pass = [&](auto pass_c) __attribute__((always_inline)) {
+            constexpr int P = decltype(pass_c)::value;
+            __syncthreads();                   // fragment reads (or the previous pass's stores) are done
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (b0 + i * bs < nrb) {
+            for (int i = 0; i < 4; ++i) {
+                if (b0 + i * bs < nrb) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = (b0 + i * bs) * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
-                if (r < rows) {
-                    const int64_t rb = (crow0 + r) * a.ldc;
-                    if constexpr (EPI == Epi::SWIGLU) {
+                    for (int e = 0; e < 16; ++e) {
+                        const int r = (b0 + i * bs) * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+                        unsigned char* row = s_ring + r * PRB;
+                        if constexpr (EPI == Epi::SWIGLU) {
 #pragma unroll
-                        for (int j = 0; j < NJ / 2; ++j) {
-                            const int col = nt * 128 + wn * (WB / 2) + j * 32 + lc;
-                            if (col < a.N)
-                                reinterpret_cast<uint16_t*>(Cb)[rb + col] =
+                            for (int j = 0; j < NJ / 2; ++j)
+                                reinterpret_cast<uint16_t*>(row)[wn * (WB / 2) + j * 32 + lc] =
                                     f32_to_bf16_bits(silu_mul_big(acc[i][j][e], acc[i][j + NJ / 2][e]));
-                        }
-                    } else {
+                        } else {
 #pragma unroll
-                        for (int j = 0; j < NJ; ++j) {
-                            const int col = nt * kBN + wn * WB + j * 32 + lc;
-                            if (col < a.N) {
-                                if (a.out_f32)
-                                    reinterpret_cast<float*>(Cb)[rb + col] = acc[i][j][e];
-                                else
-                                    reinterpret_cast<uint16_t*>(Cb)[rb + col] = f32_to_bf16_bits(acc[i][j][e]);
+                            for (int j = 0; j < NJ; ++j) {
+                                const int col = wn * WB + j * 32 - P * PC;   // the fragment's first column in the pass
+                                if (col >= 0 && col < PC) {                  // uniform: a fragment lies in one pass
+                                    if constexpr (F32)
+                                        reinterpret_cast<float*>(row)[col + lc] = acc[i][j][e];
+                                    else
+                                        reinterpret_cast<uint16_t*>(row)[col + lc] = f32_to_bf16_bits(acc[i][j][e]);
+                                }
                             }
                         }
                     }
                 }
             }
+            __syncthreads();
+            // N and ldc are multiples of 8 (checked at launch; layer sizes
+            // are multiples of 128), so a 16-byte piece is either wholly
+            // inside the output or wholly past its last column, and every
+            // piece is aligned.
+            const int c0 = nt * TC + P * PC;
+            for (int q = tid; q < rows * GPR; q += NT) {
+                const int r = q / GPR, gq = q % GPR;
+                const int col = c0 + gq * (16 / EB);
+                if (col < a.N)
+                    st16(Cb + ((crow0 + r) * a.ldc + col) * EB, *reinterpret_cast<const vec16*>(s_ring + r * PRB + gq * 16));
+            }
+        };
+        pass(std::integral_constant<int, 0>{});
+        if constexpr (F32) pass(std::integral_constant<int, 1>{});
+    };
+    if constexpr (EPI == Epi::PLAIN) {
+        if (a.out_f32) {
+            epilogue(std::true_type{});
+            return;
         }
     }
+    epilogue(std::false_type{});
 }
 
 template <Epi EPI, int NW>
@@ -303,7 +338,7 @@ GemmPlan plan_gemm_big(Epi epi, int64_t rows_upper, int n_groups, int N) {
 
 hipError_t launch_gemm_big(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     if (p.grid == 0) return hipSuccess;
-    if (a.K % kKB != 0) return hipErrorInvalidValue;
+    if (a.K % kKB != 0 || a.N % 8 != 0 || a.ldc % 8 != 0) return hipErrorInvalidValue;
     GemmArgs b = a;
     b.ksplit = 1;
     if (p.nw == 8)
