@@ -506,6 +506,12 @@ __global__ __launch_bounds__(512, 1) void gemm_big_fp8_kernel(GemmArgs a, int n_
     }
 
     // ---- epilogue -----------------------------------------------------------
+    // Outputs are staged in the (now idle) LDS ring as a row-major tile and
+    // written as whole 16-byte pieces of rows: a lane's fragment values are
+    // one column each, so direct stores would be 1-byte (e4m3 codes) or
+    // 4-byte (fp32) writes spread over 16 rows per instruction. N and ldc are
+    // multiples of 16 (checked at launch), so a piece is wholly inside the
+    // output or wholly past its last column, and aligned.
     const int64_t crow0 = shared ? m0 : static_cast<int64_t>(row0) + m0;
     if constexpr (EPI == Epi::SWIGLU) {
         // h = silu(g) * u; the tile's 128 h columns are one 1x128 scale block:
@@ -527,7 +533,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_fp8_kernel(GemmArgs a, int n_
                 for (int sft = 1; sft < 16; sft <<= 1) m = fmaxf(m, __shfl_xor(m, sft, 16));
                 if (lr == 0) s_amax[wn][wm * 128 + i * 16 + 4 * lq + v] = m;
             }
-        __syncthreads();
+        __syncthreads();                       // also: every fragment read of the ring is done
         uint8_t* Cq = static_cast<uint8_t*>(shared ? a.C_shared : a.C);
         float* Cs = static_cast<float*>(shared ? a.C_scale_shared : a.C_scale);
         const int nsb = a.N / 128;
@@ -540,50 +546,72 @@ __global__ __launch_bounds__(512, 1) void gemm_big_fp8_kernel(GemmArgs a, int n_
                     const float amax = fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
                     const bool nz = amax > 0.0f;
                     const float inv = nz ? fp8_inv_scale(amax) : 0.0f;
-                    if (r < rows) {
 #pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const int col = nt * 128 + wn * 32 + j * 16 + lr;
-                            if (col < a.N) {
-                                const uint32_t code = nz ? (cvt2_e4m3(h[i][j][v] * inv, 0.0f) & 0xffu) : 0u;
-                                Cq[(crow0 + r) * a.ldc + col] = static_cast<uint8_t>(code);
-                            }
-                        }
-                        if (wn == 0 && lr == 0) Cs[(crow0 + r) * nsb + nt] = nz ? amax / 448.0f : 1.0f;
-                    }
+                    for (int j = 0; j < 2; ++j)
+                        s_ring[r * 128 + wn * 32 + j * 16 + lr] =
+                            static_cast<uint8_t>(nz ? (cvt2_e4m3(h[i][j][v] * inv, 0.0f) & 0xffu) : 0u);
+                    if (r < rows && wn == 0 && lr == 0) Cs[(crow0 + r) * nsb + nt] = nz ? amax / 448.0f : 1.0f;
                 }
             }
+        }
+        __syncthreads();
+        for (int q = tid; q < rows * 8; q += NT) {
+            const int r = q >> 3, col = nt * 128 + (q & 7) * 16;
+            if (col < a.N) st16(Cq + (crow0 + r) * a.ldc + col, *reinterpret_cast<const vec16*>(s_ring + r * 128 + (q & 7) * 16));
         }
     } else {
         unsigned char* Cb = static_cast<unsigned char*>(shared ? a.C_shared : a.C);
+        // bf16 outputs in one pass of the tile's 256 columns, fp32 in two of
+        // 128 (128 KB of the ring each)
+        auto epilogue = [&](auto f32_out) __attribute__((always_inline)) {
+            constexpr bool F32 = decltype(f32_out)::value;
+            constexpr int EB = F32 ? 4 : 2, PC = F32 ? 128 : 256, PRB = PC * EB, GPR = PRB / 16;
+            auto pass = [&](auto pass_c) __attribute__((always_inline)) {
+                constexpr int P = decltype(pass_c)::value;
+                __syncthreads();               // fragment reads (or the previous pass's stores) are done
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (i < nbw) {
+                for (int i = 0; i < 8; ++i) {
+                    if (i < nbw) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int col = nt * 256 + wn * 64 + j * 16 + lr;
-                    if (col < a.N) {
+                        for (int j = 0; j < 4; ++j) {
+                            const int col = wn * 64 + j * 16 - P * PC;   // the fragment's first column in the pass
+                            if (col >= 0 && col < PC) {                  // uniform: a fragment lies in one pass
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int r = wm * 128 + i * 16 + 4 * lq + v;
-                            if (r < rows) {
-                                const int64_t off = (crow0 + r) * a.ldc + col;
-                                if (a.out_f32)
-                                    reinterpret_cast<float*>(Cb)[off] = acc[i][j][v];
-                                else
-                                    reinterpret_cast<uint16_t*>(Cb)[off] = f32_to_bf16_bits(acc[i][j][v]);
+                                for (int v = 0; v < 4; ++v) {
+                                    unsigned char* row = s_ring + (wm * 128 + i * 16 + 4 * lq + v) * PRB;
+                                    if constexpr (F32)
+                                        reinterpret_cast<float*>(row)[col + lr] = acc[i][j][v];
+                                    else
+                                        reinterpret_cast<uint16_t*>(row)[col + lr] = f32_to_bf16_bits(acc[i][j][v]);
+                                }
                             }
                         }
                     }
                 }
-            }
-        }
+                __syncthreads();
+                const int c0 = nt * 256 + P * PC;
+                for (int q = tid; q < rows * GPR; q += NT) {
+                    const int r = q / GPR, gq = q % GPR;
+                    const int col = c0 + gq * (16 / EB);
+                    if (col < a.N)
+                        st16(Cb + ((crow0 + r) * a.ldc + col) * EB, *reinterpret_cast<const vec16*>(s_ring + r * PRB + gq * 16));
+                }
+            };
+            pass(std::integral_constant<int, 0>{});
+            if constexpr (F32) pass(std::integral_constant<int, 1>{});
+        };
+        if (a.out_f32)
+            epilogue(std::true_type{});
+        else
+            epilogue(std::false_type{});
     }
 }
 
 template <Epi EPI>
 hipError_t launch_big_fp8(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     constexpr int lds = kBigStages * kBigStageB;
+    static_assert(lds >= 128 * 1024, "the epilogue stages 128 KB of outputs in the ring");
+    if (a.N % 16 != 0 || a.ldc % 16 != 0) return hipErrorInvalidValue;
     static std::atomic<int> lds_set[kMaxDevices];
     const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_big_fp8_kernel<EPI>), lds, lds_set);
     if (e != hipSuccess) return e;
