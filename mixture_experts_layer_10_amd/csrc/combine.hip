@@ -13,13 +13,14 @@
 //
 // One workgroup per token; each thread moves 8 consecutive hidden elements
 // per step with 16- or 32-byte accesses, so every row is read once,
-// coalesced.
+// coalesced, and the token's rows are read concurrently (kBatch at a time).
 #include "moe_device.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 128;
+constexpr int kBatch = 8;             // pairs whose rows are in flight together
 
 template <bool ROWS_F32>
 __device__ __forceinline__ void load8(const void* base, int64_t off, float (&v)[8]) {
@@ -37,6 +38,24 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float (&v)[
         for (int i = 0; i < 4; ++i) {
             v[2 * i] = bf16_bits_to_f32(static_cast<uint16_t>(a.w[i] & 0xffffu));
             v[2 * i + 1] = bf16_bits_to_f32(static_cast<uint16_t>(a.w[i] >> 16));
+        }
+    }
+}
+
+// 8 row elements from their raw 16-byte pieces (two for fp32 rows, one for bf16).
+template <bool ROWS_F32>
+__device__ __forceinline__ void unpack8(const vec16 (&raw)[ROWS_F32 ? 2 : 1], float (&v)[8]) {
+    if constexpr (ROWS_F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = __uint_as_float(raw[0].w[i]);
+            v[4 + i] = __uint_as_float(raw[ROWS_F32 ? 1 : 0].w[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0].w[i] & 0xffffu));
+            v[2 * i + 1] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0].w[i] >> 16));
         }
     }
 }
@@ -61,14 +80,34 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
         }
-        for (int j = 0; j < k; ++j) {
-            const int r = s_row[j];
-            if (r >= 0) {
-                float v[8];
-                load8<ROWS_F32>(a.rows, static_cast<int64_t>(r) * H + c, v);
-                const float wj = s_w[j];
+        // The rows of kBatch pairs are loaded, as raw 16-byte pieces, before
+        // any is used, so their memory latencies overlap. A pair with no row
+        // (inv < 0, or past k) loads row 0 (always allocated: T >= 1) and is
+        // skipped when summing; the sum runs over j in order.
+        constexpr int NV = ROWS_F32 ? 2 : 1;
+        for (int j0 = 0; j0 < k; j0 += kBatch) {
+            vec16 raw[kBatch][NV];
+            int rr[kBatch];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
+            for (int jj = 0; jj < kBatch; ++jj) {
+                rr[jj] = j0 + jj < k ? s_row[j0 + jj] : -1;
+                const int64_t off = static_cast<int64_t>(rr[jj] < 0 ? 0 : rr[jj]) * H + c;
+                if constexpr (ROWS_F32) {
+                    raw[jj][0] = ld16(static_cast<const float*>(a.rows) + off);
+                    raw[jj][NV - 1] = ld16(static_cast<const float*>(a.rows) + off + 4);
+                } else {
+                    raw[jj][0] = ld16(static_cast<const uint16_t*>(a.rows) + off);
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < kBatch; ++jj) {
+                if (rr[jj] >= 0) {
+                    float v[8];
+                    unpack8<ROWS_F32>(raw[jj], v);
+                    const float wj = s_w[j0 + jj];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
+                }
             }
         }
         if constexpr (OUT_F32) {
