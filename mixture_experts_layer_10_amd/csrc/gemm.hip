@@ -404,14 +404,22 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(GemmArgs a) {
     const int64_t stride = n;
     for (int64_t i = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4; i < n;
          i += static_cast<int64_t>(gridDim.x) * kThreads * 4) {
-        vec16 acc = ld16(a.partial + i);
+        // The slices' partial sums are loaded 8 at a time before any is
+        // added, so their memory latencies overlap (past the last slice the
+        // index is clamped and the value unused); they are added in slice
+        // order, as a plain loop over the slices would.
         float v[4];
+        for (int s0 = 0; s0 < a.ksplit; s0 += 8) {
+            vec16 p[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(acc.w[j]);
-        for (int s = 1; s < a.ksplit; ++s) {
-            const vec16 p = ld16(a.partial + s * stride + i);
+            for (int q = 0; q < 8; ++q) p[q] = ld16(a.partial + min(s0 + q, a.ksplit - 1) * stride + i);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] += __uint_as_float(p.w[j]);
+            for (int q = 0; q < 8; ++q) {
+                if (s0 + q < a.ksplit) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = s0 + q == 0 ? __uint_as_float(p[q].w[j]) : v[j] + __uint_as_float(p[q].w[j]);
+                }
+            }
         }
         if (a.bias) {
 #pragma unroll
