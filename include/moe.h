@@ -32,14 +32,15 @@
  *  - All arrays are row-major and contiguous; device pointers must be
  *    16-byte aligned.
  *  - Calls that share a workspace must not overlap on different streams.
- *  - When the routed experts get fewer than 128 rows each on average (decode
- *    shapes, bound by streaming weights), moe_expert_ffn and moe_forward run
- *    the shared expert on a second stream of the current device, forked from
- *    and joined back into `stream`, so it overlaps the routed path (in
- *    moe_forward from the router GEMM on, as it needs only x). That
- *    stream and two events are created on the first such call on a device and
- *    kept until the process ends; enqueueing on them is serialised by a lock,
- *    so calls from several host threads are safe.
+ *  - Unless both the routed experts and the shared expert take the
+ *    256 x 256 tiles (bf16 prefill shapes), moe_expert_ffn and moe_forward
+ *    run the shared expert on a second stream of the current device, so that
+ *    it overlaps the routed path: forked from `stream` (in moe_forward before
+ *    the router GEMM, as it needs only x), its down GEMM ordered after the
+ *    routed gate/up GEMM, and joined back into `stream` before its output is
+ *    read. That stream and its three events are created on the first such
+ *    call on a device and kept until the process ends; enqueueing on them is
+ *    serialised by a lock, so calls from several host threads are safe.
  */
 #ifndef MOE_H
 #define MOE_H
