@@ -235,7 +235,7 @@ enum class SharedPart { ALL, GATE_UP, DOWN };
 
 // The shared expert's down GEMM when it waits on the side stream for the
 // routed gate/up GEMM (shared_down_late): do_routed_ffn launches it right
-// after that GEMM and sets `launched`.
+// after that GEMM and sets `launched` once the join is recorded.
 struct SideStream;
 struct LateSharedDown {
     SideStream* side;
@@ -522,22 +522,25 @@ hipError_t fork_shared(const moe_config* c, int64_t T, const void* x, const moe_
     if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(ss->stream, ss->fork, 0)) != hipSuccess) return e;
     const SharedPart part = late_down ? SharedPart::GATE_UP : SharedPart::ALL;
-    if ((e = do_shared_ffn(c, T, x, wt, shared_out, ws, ss->stream, part)) != hipSuccess) return e;
-    return late_down ? hipSuccess : hipEventRecord(ss->join, ss->stream);
-}
-
-hipError_t launch_late_shared_down(LateSharedDown* d, hipStream_t s) {
-    SideStream* ss = d->side;
-    d->launched = true;
-    hipError_t e;
-    if ((e = hipEventRecord(ss->mid, s)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(ss->stream, ss->mid, 0)) != hipSuccess) return e;
-    e = do_shared_ffn(d->c, d->T, d->x, d->wt, d->shared_out, d->ws, ss->stream, SharedPart::DOWN);
+    e = do_shared_ffn(c, T, x, wt, shared_out, ws, ss->stream, part);
+    if (late_down && e == hipSuccess) return hipSuccess;       // the join follows the late down GEMM
+    // the join also follows whatever was enqueued before an error
     const hipError_t j = hipEventRecord(ss->join, ss->stream);
     return e != hipSuccess ? e : j;
 }
 
-// After a late fork whose down GEMM was never launched (an error before the
+hipError_t launch_late_shared_down(LateSharedDown* d, hipStream_t s) {
+    SideStream* ss = d->side;
+    hipError_t e = hipEventRecord(ss->mid, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->mid, 0);
+    if (e == hipSuccess) e = do_shared_ffn(d->c, d->T, d->x, d->wt, d->shared_out, d->ws, ss->stream, SharedPart::DOWN);
+    // the join follows whatever was enqueued on the side stream, also after an error
+    const hipError_t j = hipEventRecord(ss->join, ss->stream);
+    if (j == hipSuccess) d->launched = true;
+    return e != hipSuccess ? e : j;
+}
+
+// After a late fork whose join was never recorded (an error before the
 // routed gate/up GEMM), the join still has to follow the shared gate/up.
 hipError_t close_late_fork(const LateSharedDown& d) {
     return d.launched ? hipSuccess : hipEventRecord(d.side->join, d.side->stream);
@@ -591,11 +594,10 @@ hipError_t do_expert_ffn(const moe_config* c, int64_t T, const void* x, const in
     hipError_t e = do_quant_x(c, T, x, ws, s);
     if (e != hipSuccess) return e;
     const bool late = shared_down_late(c, T);
-    if (overlap_shared(c, T) && (e = fork_shared(c, T, x, wt, shared_out, ws, s, late, &side)) != hipSuccess)
-        return e;
+    if (overlap_shared(c, T)) e = fork_shared(c, T, x, wt, shared_out, ws, s, late, &side);
     LateSharedDown ld{side, c, T, x, wt, shared_out, ws, false};
-    e = do_routed_ffn(c, T, x, perm, offsets, wt, rows, ws, s, side && late ? &ld : nullptr);
-    if (side) {
+    if (e == hipSuccess) e = do_routed_ffn(c, T, x, perm, offsets, wt, rows, ws, s, side && late ? &ld : nullptr);
+    if (side) {                                                // always rejoin the side stream
         hipError_t j = late ? close_late_fork(ld) : hipSuccess;
         if (j == hipSuccess) j = join_shared(side, s);
         if (e == hipSuccess) e = j;
