@@ -203,8 +203,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
     // read; then one barrier (stage kb+1 has landed everywhere, no one reads
     // stage kb's slot any more); then the loads of stage kb+2 into that slot
     // and the reads of stage kb+1's first k-steps are issued while k-steps 2-3
-    // of stage kb run. Loads are unconditional (indices clamped), so the
-    // waits are exact; nothing past the last stage is used.
+    // of stage kb run. Every wait is for all of a thread's outstanding loads,
+    // so the last two iterations simply issue none (measured: +0.4% on the
+    // prefill layer against reloading the last stage).
     issue(0, 0);
     sync();
     issue(min(1, last), 1);
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
         read(s, 3);
         mfma(1);
         sync();
-        issue(min(kb + 2, last), s);
+        if (kb + 2 <= last) issue(kb + 2, s);     // uniform
         read(s ^ 1, 0);
         read(s ^ 1, 1);
         // raised issue priority for the MFMAs that overlap the next stage's
@@ -229,8 +230,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
         mfma(3);
         __builtin_amdgcn_s_setprio(0);
     }
-    // The clamped last loads are still landing: no direct-load write may
-    // outlive the workgroup's LDS allocation.
+    // With a single stage the prologue's second (clamped) load may still be
+    // landing: no direct-load write may outlive the workgroup's LDS.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
     // ---- epilogue: lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32)
