@@ -189,6 +189,11 @@ LAYER_CASES = {
     # gate/up on them, the down GEMM following its schedule
     "small_bf16_big_tiles": lambda: _small(T=2048, n_experts=32, expert_end=32, top_k=4, n_group=4, topk_group=2,
                                            inter=2048, shared_inter=2048, score_bias="zero"),
+    # the shared expert on 256 x 256 tiles (from 1024 tokens; ragged fifth row
+    # tile, fp32 output in two staged passes) beside the routed decode tiles
+    # (~100 rows per expert): it overlaps, its down GEMM launched behind the
+    # routed gate/up GEMM
+    "small_bf16_shared_big_late": lambda: _small(T=1100, expert_end=16, shared_inter=512),
     "small_fp8": lambda: _small(dtype="fp8", T=150, score_bias="zero"),
     "small_fp8_capacity": lambda: _small(dtype="fp8", T=300, capacity_factor=1.25, router_bias="zipf1.1",
                                          score_bias="zero"),
