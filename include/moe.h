@@ -207,7 +207,10 @@ int moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const int32_
 /* Combine (glossary step 4; infra guide section 3.1 step 4):
  *   y[t] = shared_out[t] + sum_j [inv[t,j] >= 0] * topk_w[t,j] * out_rows[inv[t,j]]
  * summed in fp32; dropped and non-local pairs add nothing (no renormalisation).
- * y [T, H] device out in cfg->out_dtype; shared_out [T, H] fp32 or NULL. */
+ * out_rows [T*k, H] as moe_expert_ffn writes it: all T*k rows must be
+ * allocated, since the kernel may read row 0 (and discard it) for a pair
+ * with no row. y [T, H] device out in cfg->out_dtype; shared_out [T, H] fp32
+ * or NULL. */
 int moe_combine(const moe_config* cfg, int64_t T, const void* out_rows, const int32_t* inv,
                 const float* topk_w, const void* shared_out, void* y, hipStream_t stream);
 
