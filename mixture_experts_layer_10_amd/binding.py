@@ -280,7 +280,7 @@ def moe_combine(cfg, out_rows, inv, topk_w, shared_out, y, stream=None):
     k = cfg.top_k
     rd = _row_dtype(cfg)
     _check(lib().moe_combine(
-        ctypes.byref(cfg), T, _ptr(out_rows, rd, None, "out_rows"), _ptr(inv, torch.int32, (T * k,), "inv"),
+        ctypes.byref(cfg), T, _ptr(out_rows, rd, (T * k, H), "out_rows"), _ptr(inv, torch.int32, (T * k,), "inv"),
         _ptr(topk_w, torch.float32, (T, k), "topk_w"),
         _ptr(shared_out, torch.float32, (T, H), "shared_out", optional=True),
         _ptr(y, _out_dtype(cfg), (T, H), "y"), _stream(stream)), "moe_combine")
