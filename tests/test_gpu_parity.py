@@ -295,6 +295,22 @@ def check_layer(w, name):
             assert _rel(host(r["shared"]), ref["shared"]) < tol
     err = _rel(host(r["y"]), ref["y"])
     say("  max|dy|/rms =", err)
+    if w["dtype"] != "f32" and R:
+        # y sums the gated expert rows, and each row element may sit one bf16
+        # step apart on the two sides (the straddle allowed for the rows
+        # above): allow sum_j |w_tj| 2**-7 |row element| on top of the
+        # tolerance. It matters where y is small against the rows it sums
+        # (no shared expert, few tokens with a local expert).
+        yg, yw = host(r["y"]).astype(np.float64), np.asarray(ref["y"], dtype=np.float64)
+        inv, gate = np.asarray(ref["inv"]).reshape(yw.shape[0], -1), np.asarray(ref["w"], dtype=np.float64)
+        mag = np.abs(np.asarray(ref["rows"], dtype=np.float64))
+        slack = np.zeros_like(yw)
+        for j in range(inv.shape[1]):
+            kept = inv[:, j] >= 0
+            slack[kept] += np.abs(gate[kept, j])[:, None] * 2.0 ** -7 * mag[inv[kept, j]]
+        rms_y = math.sqrt(float(np.mean(yw * yw)))
+        err = float(np.max(np.maximum(np.abs(yg - yw) - slack, 0.0))) / rms_y if rms_y > 0 else err
+        say("  with the rows' bf16 step allowed:", err)
     assert err < tol
     # the fused entry point gives the same result as the stage calls
     lo = torch.empty_like(r["logits"])
