@@ -194,6 +194,11 @@ LAYER_CASES = {
     # (~100 rows per expert): it overlaps, its down GEMM launched behind the
     # routed gate/up GEMM
     "small_bf16_shared_big_late": lambda: _small(T=1100, expert_end=16, shared_inter=512),
+    # top-1 routing, no shared expert, a 5-of-16 local share: most tokens' y
+    # is exactly 0, so y is small against the expert rows it sums
+    "small_bf16_top1_sparse_share": lambda: _small(T=284, hidden=1024, n_experts=16, expert_begin=1, expert_end=6,
+                                                   top_k=1, n_group=8, topk_group=3, renormalize=False, inter=640,
+                                                   shared_inter=0, router_bias="zipf1.1"),
     "small_fp8": lambda: _small(dtype="fp8", T=150, score_bias="zero"),
     "small_fp8_capacity": lambda: _small(dtype="fp8", T=300, capacity_factor=1.25, router_bias="zipf1.1",
                                          score_bias="zero"),
