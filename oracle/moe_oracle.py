@@ -46,7 +46,7 @@ combine exchange carries BF16, infra guide
 section 3.2). The shared expert's output never leaves the token's GPU and is
 kept unrounded.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   * group score = sum of the two largest selection scores in the group;
   * ties (experts and groups) go to the lower index; slots hold experts in
     selection order (descending score);
