@@ -29,6 +29,11 @@
  *    device data on the host, so calls can be captured in a HIP graph.
  *  - Arguments are validated before anything is enqueued: a nonzero return
  *    means nothing was launched. T == 0 is a successful no-op.
+ *  - The GEMMs address operand rows with 32-bit byte offsets: a call whose
+ *    x [T, H], intermediate rows [T k, I] or [T, I_s], router weight [E, H]
+ *    or one expert's [2 I, H] weights would span more than 4 GiB (counted at
+ *    4 bytes per element for F32, 2 otherwise) returns MOE_ERR_UNSUPPORTED
+ *    (DeepSeek-V3 bf16 shape: from T = 131,073 tokens in one call).
  *  - All arrays are row-major and contiguous; device pointers must be
  *    16-byte aligned.
  *  - Calls that share a workspace must not overlap on different streams.

@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <unordered_map>
@@ -32,6 +33,8 @@ int validate(const moe_config* c) {
     if (c->n_group <= 0 || c->n_experts % c->n_group != 0) return MOE_ERR_INVALID_ARG;
     if (c->topk_group <= 0 || c->topk_group > c->n_group) return MOE_ERR_INVALID_ARG;
     if (c->top_k > c->topk_group * (c->n_experts / c->n_group)) return MOE_ERR_INVALID_ARG;
+    // a group is scored by the sum of its two best experts: it needs two
+    if (c->n_group > 1 && c->n_experts / c->n_group < 2) return MOE_ERR_INVALID_ARG;
     if (c->expert_begin < 0 || c->expert_end <= c->expert_begin || c->expert_end > c->n_experts)
         return MOE_ERR_INVALID_ARG;
     if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
@@ -53,6 +56,26 @@ int validate(const moe_config* c) {
 
 int act_bytes(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 4 : c->dtype == MOE_DTYPE_BF16 ? 2 : 1; }
 int row_bytes(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 4 : 2; }
+
+// The GEMM kernels address a row of an operand as row * K * element bytes in
+// 32 bits (the base pointer carries the rest), so no operand they read may
+// span more than 4 GiB: the gathered hidden states x [T, H], the intermediate rows
+// h [T k, I] and h_shared [T, I_s], the router weight [E, H] and one
+// expert's stacked weights [2 I, H] (bf16 bytes for the e4m3 and FP4 paths,
+// which is an upper bound of their own). `router_only`: the router GEMM's
+// operands alone.
+bool offsets_fit(const moe_config* c, int64_t T, bool router_only) {
+    const int64_t eb = c->dtype == MOE_DTYPE_F32 ? 4 : 2;
+    const int64_t lim = int64_t{1} << 32;
+    const int64_t H = c->hidden;
+    int64_t need = std::max(T * H, static_cast<int64_t>(c->n_experts) * H);
+    if (!router_only) {
+        need = std::max(need, T * c->top_k * static_cast<int64_t>(c->inter));
+        need = std::max(need, T * static_cast<int64_t>(c->shared_inter));
+        need = std::max(need, 2 * static_cast<int64_t>(std::max(c->inter, c->shared_inter)) * H);
+    }
+    return need * eb <= lim;     // the last row starts below 4 GiB and ends at most there
+}
 Elem gemm_elem(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? Elem::F32 : Elem::BF16; }
 
 // Expert GEMMs on e4m3 activations: FP8 block-scaled or MX (FP4 weights).
@@ -678,6 +701,7 @@ int moe_router_gemm(const moe_config* cfg, int64_t T, const void* x, const void*
     if (T == 0) return MOE_OK;
     if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits)) return MOE_ERR_MISALIGNED;
+    if (!offsets_fit(cfg, T, true)) return MOE_ERR_UNSUPPORTED;
     if ((st = check_ws(cfg, T, ws, ws_bytes))) return st;
     return hip_status(do_router_gemm(cfg, T, x, w_router, router_bias, logits, ws, stream));
 }
@@ -719,6 +743,7 @@ int moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const int32_
     if (!aligned16(x) || !aligned16(perm) || !aligned16(offsets) || !aligned16(out_rows) ||
         (shared_out && !aligned16(shared_out)))
         return MOE_ERR_MISALIGNED;
+    if (!offsets_fit(cfg, T, false)) return MOE_ERR_UNSUPPORTED;
     if ((st = check_ws(cfg, T, ws, ws_bytes))) return st;
     return hip_status(do_expert_ffn(cfg, T, x, perm, offsets, weights, out_rows, shared_out, ws, stream));
 }
@@ -747,6 +772,7 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
     if (!aligned16(x) || !aligned16(w_router) || !aligned16(y) || (logits_out && !aligned16(logits_out)) ||
         (topk_ids_out && !aligned16(topk_ids_out)))
         return MOE_ERR_MISALIGNED;
+    if (!offsets_fit(cfg, T, false)) return MOE_ERR_UNSUPPORTED;
     if ((st = check_ws(cfg, T, ws, ws_bytes))) return st;
     const Layout L = layout(cfg, T);
     float* logits = logits_out ? logits_out : at<float>(ws, L.logits);

@@ -61,6 +61,9 @@ def _good(**kw):
     (dict(dtype="mxfp4", hidden=7168 + 128), B.ERR_UNSUPPORTED),   # FP4 GEMM: K chunks of 256
     (dict(dtype="mxfp4", inter=2048 + 128), B.ERR_UNSUPPORTED),
     (dict(dtype="mxfp4", shared_inter=384), B.ERR_UNSUPPORTED),
+    # a group is scored by its two best experts: one expert per group is refused
+    (dict(n_experts=8, expert_end=8, n_group=8, topk_group=4, top_k=2), B.ERR_INVALID_ARG),
+    (dict(n_experts=16, expert_end=16, n_group=8, topk_group=4, top_k=2), B.OK),
 ])
 def test_validate_config(kw, status):
     assert moe.validate_config(_good(**kw)) == status
@@ -161,6 +164,31 @@ def test_stage_calls_reject_before_launch():
     bad = _good(n_group=7)
     assert L.moe_forward(ctypes.byref(bad), 4, FAKE, FAKE, None, None, ctypes.byref(W), FAKE, None, None,
                          FAKE, need, None) == B.ERR_INVALID_ARG
+
+
+def test_operands_past_4_gib_are_refused():
+    """The GEMMs address operand rows with 32-bit byte offsets: a batch whose
+    intermediate rows h [T k, I] reach 4 GiB (DeepSeek bf16 shape, k = 8,
+    I = 2048: from T = 131,072 + 1) is refused before anything is launched,
+    by the whole layer and by the expert stage; the router GEMM alone is
+    refused once x [T, H] reaches 4 GiB."""
+    L = moe.lib()
+    c = _good(expert_end=256)
+    cp = ctypes.byref(c)
+    W = B.Weights()
+    W.w13 = W.w2 = W.shared_w13 = W.shared_w2 = FAKE
+    for T, ok in ((131072, True), (131073, False)):
+        need = moe.workspace_bytes(c, T)
+        want_ws = B.ERR_WORKSPACE_TOO_SMALL if ok else B.ERR_UNSUPPORTED
+        # a one-byte workspace: a batch that fits gets as far as the workspace check
+        assert L.moe_forward(cp, T, FAKE, FAKE, None, None, ctypes.byref(W), FAKE, None, None, FAKE, 1,
+                             None) == want_ws
+        assert L.moe_expert_ffn(cp, T, FAKE, FAKE, FAKE, ctypes.byref(W), FAKE, FAKE, FAKE, 1, None) == want_ws
+        assert need > 1
+    # the router GEMM reads only x and the router weight: x [T, 7168] bf16 reaches 4 GiB at T = 299,594
+    for T, ok in ((299593, True), (299594, False)):
+        st = L.moe_router_gemm(cp, T, FAKE, FAKE, None, FAKE, FAKE, 1, None)
+        assert st == (B.ERR_WORKSPACE_TOO_SMALL if ok else B.ERR_UNSUPPORTED)
 
 
 def test_binding_requires_gpu_tensors():
