@@ -1,12 +1,16 @@
 """Benchmark of the MoE layer forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config NAME]
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--also NAME,...]
 
 A step is one moe_forward call (router GEMM, top-k, dispatch, grouped-GEMM
 experts + shared expert, combine) over one batch of seeded synthetic tokens
-resident in HBM. Prints one JSON line with tokens/s, the roofline of the
-dominant kernel (measured with HIP events over the timed steps) and the CPU
-oracle timed on a bounded sample of the same workload.
+resident in HBM. The headline workload is the whole 256-expert DeepSeek-V3
+layer at prefill shape (16384 tokens, bf16), where the grouped GEMM is bound
+by the matrix cores; the same line carries a second measured block for the
+decode shape (512 tokens), where it is bound by streaming the expert weights.
+Prints one JSON line with tokens/s, the roofline of the dominant kernel
+(measured with HIP events over the timed steps) and the CPU oracle timed on a
+bounded sample of the headline workload.
 """
 import argparse
 import hashlib
@@ -33,9 +37,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="ep8_decode_bf16")
+    ap.add_argument("--config", default="full_prefill_bf16")
+    ap.add_argument("--also", default="full_decode_bf16",
+                    help="comma-separated workloads measured after the headline one and reported in the same "
+                         "line under 'also' ('none' for none)")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
-    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens of the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="capture the timed steps in one HIP graph and replay it (no launch gaps)")
@@ -178,7 +185,12 @@ def stage_bytes_flops(w, counts, stage):
 
 def cpu_baseline(w, inp, sample, min_seconds=10.0):
     """The oracle as it stands, timed on the first `sample` tokens of the
-    batch, in passes repeated until at least `min_seconds` have elapsed."""
+    batch (a batch of its own: router GEMM, top-k, dispatch, one expert at a
+    time, shared expert, combine), in passes repeated until at least
+    `min_seconds` have elapsed. Its matmuls run in float32 (BLAS), the
+    arithmetic type a CPU implementation of the bf16 layer would use; the
+    weights are made resident in host memory as float32 beforehand (untimed,
+    one expert at a time from the device)."""
     import platform
     import torch
     from oracle import moe_oracle as O
@@ -186,10 +198,14 @@ def cpu_baseline(w, inp, sample, min_seconds=10.0):
     def h(t):
         if t is None:
             return None
-        t = t.detach().cpu()
         if t.dtype == torch.float8_e4m3fn:
-            return t.view(torch.uint8).numpy()
-        return t.numpy() if t.dtype == torch.uint8 else t.float().numpy()
+            return t.detach().cpu().view(torch.uint8).numpy()
+        if t.dtype == torch.uint8:
+            return t.detach().cpu().numpy()
+        return t.detach().float().cpu().numpy()
+
+    def experts(t):
+        return None if t is None else [h(t[e]) for e in range(t.shape[0])]
 
     cfg = O.Config.from_workload(w)
     S = min(sample, w["T"])
@@ -197,11 +213,11 @@ def cpu_baseline(w, inp, sample, min_seconds=10.0):
     args = dict(router_bias=h(inp["router_bias"]), score_bias=h(inp["score_bias"]),
                 shared_w13=h(inp["shared_w13"]), shared_w2=h(inp["shared_w2"]))
     scales = {k: h(inp.get(k)) for k in ("w13_scale", "w2_scale", "shared_w13_scale", "shared_w2_scale")}
-    wr, w13, w2 = h(inp["w_router"]), h(inp["w13"]), h(inp["w2"])
+    wr, w13, w2 = h(inp["w_router"]), experts(inp["w13"]), experts(inp["w2"])
     passes = 0
     t0 = time.perf_counter()
     while True:
-        O.forward(cfg, x, wr, w13, w2, scales=scales, **args)
+        O.forward(cfg, x, wr, w13, w2, scales=scales, work=np.float32, **args)
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
@@ -222,28 +238,26 @@ def cpu_baseline(w, inp, sample, min_seconds=10.0):
             cpu = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
     except (OSError, StopIteration):
         pass
+    del w13, w2
     return {"value": passes * S / dt, "unit": "tokens/s", "cores": blas_threads or cores, "kind": "oracle",
-            "sample": f"first {S} of {w['T']} tokens of the same workload, whole layer (router GEMM, top-k, "
-                      f"dispatch, experts, shared expert, combine), {passes} passes in {dt:.1f} s wall",
+            "sample": f"first {S} of {w['T']} tokens of the {w['name']} workload as a batch of their own, whole "
+                      f"layer (router GEMM, top-k, dispatch, every local expert, shared expert, combine), float32 "
+                      f"BLAS matmuls, {passes} passes in {dt:.1f} s wall",
             "affinity_cores": cores, "cpu": cpu, "blas": blas}
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU: --gpus {a.gpus} is not supported by this build "
-              "(the layer runs one GPU's share of experts; no collectives).", file=sys.stderr)
-        sys.exit(2)
-    if a.calibrate_copy:
-        calibrate_copy(a.calibrate_copy)
-        return
+def measure(name, a, peaks=None):
+    """Time moe_forward on workload `name`: tokens/s over the timed steps, the
+    dominant kernel's roofline from HIP events over those steps, the grouped
+    GEMM's fractions and a per-stage breakdown from an untimed pass.
+    Returns (result dict, inputs)."""
     import torch
     import mixture_experts_layer_10_amd as moe
     from synth import make_inputs, workload
 
-    w = workload(a.config)
+    w = workload(name)
     T = w["T"]
-    print(f"[bench] config {a.config}: T={T} H={w['hidden']} E={w['n_experts']} "
+    print(f"[bench] workload {name}: T={T} H={w['hidden']} E={w['n_experts']} "
           f"local=[{w['expert_begin']},{w['expert_end']}) dtype={w['dtype']}", file=sys.stderr, flush=True)
     inp = make_inputs(w, device="cuda")
     cfg = moe.config_from_workload(w, out_dtype=a.out_dtype)
@@ -336,7 +350,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": peak_mfma, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(dom, a.config, w["dtype"])
+    roof["traffic"] = stored_traffic(dom, name, w["dtype"])
     family = {"fp8": "gemm_fp8_kernel", "mxfp4": "gemm_mx_kernel"}.get(w["dtype"], "gemm_kernel / gemm_big_kernel")
     roof["kernel"] = f"{family} ({dom})"
     roof["kernel_ms"] = t_dom * 1e3
@@ -354,6 +368,14 @@ def main():
     gt = (stage_ms["gate_up"] + stage_ms["down"]) * 1e-3
     grouped = {"ms": gt * 1e3, "hbm_frac": gb / gt / 1e9 / PEAK_HBM_GBS,
                "mfma_frac": gf / gt / 1e12 / peak_mfma}
+    if peaks:
+        grouped["hbm_frac_of_stream_read"] = gb / gt / 1e9 / peaks["stream_read_gbs"]
+        if w["dtype"] == "bf16":
+            grouped["mfma_frac_of_loop"] = gf / gt / 1e12 / peaks["mfma_loop_bf16_tflops"]
+        if roof["unit"] == "GB/s":
+            roof["frac_of_stream_read"] = roof["achieved"] / peaks["stream_read_gbs"]
+        elif w["dtype"] == "bf16":
+            roof["frac_of_mfma_loop"] = roof["achieved"] / peaks["mfma_loop_bf16_tflops"]
 
     # expert load of this batch over all routed experts (device counts),
     # and how an 8-GPU expert-parallel placement would balance it
@@ -366,36 +388,51 @@ def main():
                    "ep8_contiguous_imbalance": float(contig.max() / contig.mean()),
                    "ep8_replanned_imbalance": moe.moe_eplb_plan(lc, 8, 0)[3],
                    "ep8_replanned_8_redundant_imbalance": moe.moe_eplb_plan(lc, 8, 8)[3]}
-
-    peaks = None
-    if not a.no_peaks:
-        peaks = achievable_peaks()
-        if roof["unit"] == "GB/s":
-            peaks["dominant_frac_of_achievable"] = roof["achieved"] / peaks["stream_read_gbs"]
-        elif w["dtype"] == "bf16":
-            peaks["dominant_frac_of_achievable"] = roof["achieved"] / peaks["mfma_loop_bf16_tflops"]
-        grouped["hbm_frac_of_stream_read"] = gb / gt / 1e9 / peaks["stream_read_gbs"]
-        if w["dtype"] == "bf16":
-            grouped["mfma_frac_of_loop"] = gf / gt / 1e12 / peaks["mfma_loop_bf16_tflops"]
-
-    out = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic",
-        "config": {"workload": a.config, "tokens": T, "hidden": w["hidden"], "experts": w["n_experts"],
+    res = {
+        "value": value, "unit": "tokens/s", "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "dtype": w["dtype"],
+        "config": {"workload": name, "tokens": T, "hidden": w["hidden"], "experts": w["n_experts"],
                    "local_experts": [w["expert_begin"], w["expert_end"]], "top_k": w["top_k"],
                    "inter": w["inter"], "shared_inter": w["shared_inter"], "out_dtype": a.out_dtype},
-        "roofline": roof,
-        "grouped_gemm": grouped,
-        "stage_ms": stage_ms,
-        "step_ms": step_pct,
-        "achievable": peaks,
-        "rows": int(counts.sum()), "max_rows_per_expert": int(counts.max()),
-        "expert_load": expert_load,
+        "roofline": roof, "grouped_gemm": grouped, "stage_ms": stage_ms, "step_ms": step_pct,
+        "rows": int(counts.sum()), "max_rows_per_expert": int(counts.max()), "expert_load": expert_load,
     }
+    del W, ws, y
+    return res, (w, inp)
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU: --gpus {a.gpus} is not supported by this build "
+              "(the layer runs one GPU's share of experts; no collectives).", file=sys.stderr)
+        sys.exit(2)
+    if a.calibrate_copy:
+        calibrate_copy(a.calibrate_copy)
+        return
+    import torch
+
+    peaks = None if a.no_peaks else achievable_peaks()
+    head, (w, inp) = measure(a.config, a, peaks)
+    out = {"metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+           "warmup": a.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic", "config": head["config"]}
+    for key in ("roofline", "grouped_gemm", "stage_ms", "step_ms", "rows", "max_rows_per_expert", "expert_load"):
+        out[key] = head[key]
+    out["achievable"] = peaks
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_sample)
+    del inp
+    torch.cuda.empty_cache()
+    also = [n for n in a.also.split(",") if n and n != "none" and n != a.config]
+    if also:
+        out["also"] = {}
+        for n in also:
+            res, (_, inp2) = measure(n, a, peaks)
+            del inp2
+            torch.cuda.empty_cache()
+            out["also"][n] = res
     print(json.dumps(out), flush=True)
 
 

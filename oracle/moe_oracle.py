@@ -311,9 +311,11 @@ def dequant_mx_rows(q, scale_codes):
 # Stage 1: router GEMM
 # ---------------------------------------------------------------------------
 
-def router_logits(x, w_router, router_bias=None):
-    """logits = x W_r^T (+ c), in fp64 (returned as float64)."""
-    l = np.asarray(x, dtype=np.float64) @ np.asarray(w_router, dtype=np.float64).T
+def router_logits(x, w_router, router_bias=None, work=np.float64):
+    """logits = x W_r^T (+ c), in fp64 (returned as float64). `work` is the
+    matmul's arithmetic type: fp64 for every parity use; the CPU baseline
+    timing alone passes float32."""
+    l = (np.asarray(x, dtype=work) @ np.asarray(w_router, dtype=work).T).astype(np.float64)
     if router_bias is not None:
         l = l + np.asarray(router_bias, dtype=np.float64)[None, :]
     return l
@@ -460,7 +462,7 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def swiglu_expert(cfg, x_rows, w13, w2, inter, w13_scale=None, w2_scale=None, round_out=True):
+def swiglu_expert(cfg, x_rows, w13, w2, inter, w13_scale=None, w2_scale=None, round_out=True, work=np.float64):
     """o = (silu(x W_g^T) * (x W_u^T)) W_d^T for the given rows.
 
     x_rows: [n, H] input rows (their exact stored values). w13: [2I, H] with
@@ -471,6 +473,8 @@ def swiglu_expert(cfg, x_rows, w13, w2, inter, w13_scale=None, w2_scale=None, ro
     the activations are MX e4m3 (32-element power-of-two scales). Returns fp64 [n, H]; with
     round_out (routed experts, whose outputs travel through the combine) the
     rows are rounded to their bf16 carrier when activations are bf16 or fp8.
+    `work` is the matmuls' arithmetic type: fp64 for every parity use; the CPU
+    baseline timing alone passes float32.
     """
     if cfg.act == "fp8":
         W13 = dequant_block_weight(w13, w13_scale)
@@ -482,11 +486,12 @@ def swiglu_expert(cfg, x_rows, w13, w2, inter, w13_scale=None, w2_scale=None, ro
         W2 = dequant_mx_weight(w2, w2_scale)
         xa = dequant_mx_rows(*quantize_mx_rows(np.asarray(x_rows, dtype=F32)))
     else:
-        W13 = np.asarray(w13, dtype=np.float64)
-        W2 = np.asarray(w2, dtype=np.float64)
-        xa = np.asarray(x_rows, dtype=np.float64)
-    g = xa @ W13[:inter].T
-    u = xa @ W13[inter:].T
+        W13 = np.asarray(w13, dtype=work)
+        W2 = np.asarray(w2, dtype=work)
+        xa = np.asarray(x_rows, dtype=work)
+    W13, W2, xa = W13.astype(work, copy=False), W2.astype(work, copy=False), xa.astype(work, copy=False)
+    g = (xa @ W13[:inter].T).astype(np.float64)
+    u = (xa @ W13[inter:].T).astype(np.float64)
     h = silu(g) * u
     if cfg.act == "fp8":
         qh, sh = quantize_fp8_rows(h.astype(F32))
@@ -495,7 +500,7 @@ def swiglu_expert(cfg, x_rows, w13, w2, inter, w13_scale=None, w2_scale=None, ro
         ha = dequant_mx_rows(*quantize_mx_rows(h.astype(F32)))
     else:
         ha = _round_act(h, cfg.act)
-    o = ha @ W2.T
+    o = (ha.astype(work, copy=False) @ W2.T).astype(np.float64)
     if round_out and cfg.act in ("bf16", "fp8", "mxfp4"):
         o = bf16_round(o)
     return o
@@ -524,7 +529,7 @@ def combine(cfg, T, out_rows, inv, w, shared=None):
 # Whole layer
 # ---------------------------------------------------------------------------
 
-def experts_forward(cfg, x, disp, w13, w2, w13_scale=None, w2_scale=None):
+def experts_forward(cfg, x, disp, w13, w2, w13_scale=None, w2_scale=None, work=np.float64):
     """Expert output rows [R, H] in dispatch order (one expert at a time)."""
     x = np.asarray(x)
     k = cfg.top_k
@@ -537,33 +542,35 @@ def experts_forward(cfg, x, disp, w13, w2, w13_scale=None, w2_scale=None):
         tok = disp["perm"][a:b] // k
         out[a:b] = swiglu_expert(cfg, x[tok], w13[le], w2[le], cfg.inter,
                                  None if w13_scale is None else w13_scale[le],
-                                 None if w2_scale is None else w2_scale[le])
+                                 None if w2_scale is None else w2_scale[le], work=work)
     return out
 
 
-def shared_forward(cfg, x, sw13, sw2, sw13_scale=None, sw2_scale=None):
+def shared_forward(cfg, x, sw13, sw2, sw13_scale=None, sw2_scale=None, work=np.float64):
     if cfg.shared_inter <= 0:
         return None
     # The shared expert's output stays on the token's own GPU: no bf16 carrier.
-    return swiglu_expert(cfg, x, sw13, sw2, cfg.shared_inter, sw13_scale, sw2_scale, round_out=False)
+    return swiglu_expert(cfg, x, sw13, sw2, cfg.shared_inter, sw13_scale, sw2_scale, round_out=False, work=work)
 
 
 def forward(cfg, x, w_router, w13, w2, router_bias=None, score_bias=None,
-            shared_w13=None, shared_w2=None, logits=None, scales=None):
+            shared_w13=None, shared_w2=None, logits=None, scales=None, work=np.float64):
     """The whole layer. If `logits` (float32 [T, E]) is given it is used for
     routing instead of the oracle's own router GEMM. `scales` holds the fp8
     block scales dict (w13_scale, w2_scale, shared_w13_scale, shared_w2_scale).
-    Returns dict with y (fp64 [T, H]) and every intermediate."""
+    `work`: the matmuls' arithmetic type (fp64 for parity; float32 only for
+    the CPU baseline timing). Returns dict with y (fp64 [T, H]) and every
+    intermediate."""
     scales = scales or {}
     x = np.asarray(x)
     T = x.shape[0]
-    own_logits = router_logits(x, w_router, router_bias)
+    own_logits = router_logits(x, w_router, router_bias, work=work)
     l32 = own_logits.astype(F32) if logits is None else np.asarray(logits, dtype=F32)
     ids, w = route(cfg, l32, score_bias)
     disp = dispatch(cfg, ids)
-    rows = experts_forward(cfg, x, disp, w13, w2, scales.get("w13_scale"), scales.get("w2_scale"))
+    rows = experts_forward(cfg, x, disp, w13, w2, scales.get("w13_scale"), scales.get("w2_scale"), work=work)
     sh = shared_forward(cfg, x, shared_w13, shared_w2,
-                        scales.get("shared_w13_scale"), scales.get("shared_w2_scale"))
+                        scales.get("shared_w13_scale"), scales.get("shared_w2_scale"), work=work)
     y = combine(cfg, T, rows, disp["inv"], w, sh)
     return dict(y=y, logits=own_logits, ids=ids, w=w, rows=rows, shared=sh, **disp)
 

@@ -19,7 +19,7 @@ import mixture_experts_layer_10_amd as moe
 from oracle import moe_oracle as O
 from synth import make_inputs, workload
 
-from gpu_helpers import TOL, host, say
+from gpu_helpers import TOL, check_rows, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -102,3 +102,47 @@ def test_full_size_forward(name):
     err = O.rel_max_err(host(y)[tok], want_y)
     say("  max|dy|/rms on the sample =", err)
     assert err < TOL[w["dtype"]]
+
+    # whole expert groups: the routed rows of several experts, every row,
+    # against the oracle's expert FFN on the same gathered tokens
+    say("  moe_expert_ffn at full size")
+    rd = torch.bfloat16 if w["dtype"] != "f32" else torch.float32
+    rows = torch.empty(T * k, H, dtype=rd, device="cuda")
+    shared = torch.empty(T, H, dtype=torch.float32, device="cuda") if w["shared_inter"] else None
+    moe.moe_expert_ffn(cfg, inp["x"], d["perm"], d["offsets"], Wt, rows, shared, ws)
+    torch.cuda.synchronize()
+    offs = ref_d["offsets"]
+    for le in _groups_to_check(ref_d):
+        a, b = int(offs[le]), int(offs[le + 1])
+        idx = _rows_to_check(b - a)
+        say(f"  expert {le}: {b - a} rows (raw {int(ref_d['raw_counts'][le])}), checking {len(idx)}")
+        toks = ref_d["perm"][a:b][idx] // k
+        w13, w2, s13, s2 = get_expert(le)
+        want = O.swiglu_expert(ocfg, host(inp["x"][torch.from_numpy(toks).cuda()]), w13, w2, w["inter"], s13, s2)
+        got = host(rows[a:b])[idx].astype(np.float64)
+        check_rows(got, want, w["dtype"])
+
+
+def _groups_to_check(d):
+    """The largest group; the largest whose row count is not a multiple of 32
+    (a ragged last row block); a capacity-capped group, if any; the smallest
+    non-empty group."""
+    counts, raw = d["counts"], d["raw_counts"]
+    pick = [int(np.argmax(counts))]
+    ragged = np.nonzero(counts % 32)[0]
+    if len(ragged):
+        pick.append(int(ragged[np.argmax(counts[ragged])]))
+    capped = np.nonzero(raw > counts)[0]
+    if len(capped):
+        pick.append(int(capped[0]))
+    nz = np.nonzero(counts)[0]
+    pick.append(int(nz[np.argmin(counts[nz])]))
+    return list(dict.fromkeys(pick))
+
+
+def _rows_to_check(n):
+    """Every row of a group up to 1024 rows; beyond that the first 256 and the
+    last 256 (first and last row tiles)."""
+    if n <= 1024:
+        return np.arange(n)
+    return np.concatenate([np.arange(256), np.arange(n - 256, n)])

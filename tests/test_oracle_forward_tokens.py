@@ -229,3 +229,22 @@ def test_planted_router_bias_mistakes_are_caught(old, new):
     except ValueError:
         return                                                   # a shape error is caught too
     assert not np.allclose(got, want.numpy(), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_float32_work_type_stays_within_tolerance(dtype):
+    """The CPU baseline times the oracle with float32 matmuls; that variant
+    routes identically and stays well within the layer tolerance of the fp64
+    oracle (it is never used for parity)."""
+    w = _tiny(dtype=dtype, capacity_factor=1.25, router_bias="zipf1.1", score_bias="zero", T=48)
+    inp = make_inputs(w)
+    cfg = O.Config.from_workload(w)
+    h = {k: _np(v) for k, v in inp.items()}
+    scales = {k: h.get(k) for k in ("w13_scale", "w2_scale", "shared_w13_scale", "shared_w2_scale")}
+    args = (cfg, h["x"], h["w_router"], h["w13"], h["w2"])
+    kw = dict(router_bias=h["router_bias"], score_bias=h["score_bias"], shared_w13=h["shared_w13"],
+              shared_w2=h["shared_w2"], scales=scales)
+    ref = O.forward(*args, **kw)
+    got = O.forward(*args, work=np.float32, **kw)
+    assert np.array_equal(got["ids"], ref["ids"])
+    assert O.rel_max_err(got["y"], ref["y"]) < 0.2 * {"bf16": 2e-2, "fp8": 6e-2}[dtype]
