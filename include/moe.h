@@ -251,6 +251,25 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
                 void* y, float* logits_out, int32_t* topk_ids_out,
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_forward_noalloc: moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid it). Same arguments and result as moe_forward, less the workspace:
+ * the layer's scratch lives in a device array of the library's own, of
+ * MOE_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends. A
+ * batch whose workspace (moe_workspace_bytes) exceeds that returns
+ * MOE_ERR_WORKSPACE_TOO_SMALL before anything is launched (DeepSeek-V3 bf16
+ * shape: up to 339 tokens per call). The call allocates nothing and
+ * creates no stream or event: the shared expert runs on `stream` after the
+ * routed experts, with the kernels moe_forward uses, so y equals
+ * moe_forward's bit for bit. The array's device address is looked up once
+ * per device, on the first call with that device current. All calls on one
+ * GPU share its array: calls that overlap on one GPU (two streams, or two
+ * host threads) race, and must be ordered by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                        const float* router_bias, const float* score_bias, const moe_weights* weights,
+                        void* y, float* logits_out, int32_t* topk_ids_out, hipStream_t stream);
+
 /* ---- Expert load statistics and placement ----------------------------------
  * Infra guide "Data parallelism and expert parallelism", section 5: under
  * expert parallelism every layer waits for the GPU that received the most

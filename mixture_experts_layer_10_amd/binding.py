@@ -70,6 +70,7 @@ def lib():
             "moe_expert_ffn": (ctypes.c_int, [cfgp, i64, vp, i32p, i32p, wp, vp, vp, vp, ctypes.c_size_t, vp]),
             "moe_combine": (ctypes.c_int, [cfgp, i64, vp, i32p, fp, vp, vp, vp]),
             "moe_forward": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, wp, vp, fp, i32p, vp, ctypes.c_size_t, vp]),
+            "moe_forward_noalloc": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, wp, vp, fp, i32p, vp]),
             "moe_quantize_fp8": (ctypes.c_int, [cfgp, i64, vp, vp, fp, vp]),
             "moe_quantize_mx": (ctypes.c_int, [cfgp, i64, vp, vp, vp, vp]),
             "moe_expert_load": (ctypes.c_int, [cfgp, i64, vp, vp, vp]),
@@ -317,6 +318,26 @@ def moe_forward(cfg, x, w_router, router_bias, score_bias, weights, y, ws, logit
         _ptr(logits_out, torch.float32, (T, E), "logits_out", optional=True),
         _ptr(topk_ids_out, torch.int32, (T, cfg.top_k), "topk_ids_out", optional=True),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream)), "moe_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20      # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc(cfg, x, w_router, router_bias, score_bias, weights, y, logits_out=None,
+                        topk_ids_out=None, stream=None):
+    """moe_forward without a workspace: the library's own per-GPU scratch
+    array (MOE_NOALLOC_SCRATCH_BYTES) serves instead; nothing is allocated."""
+    T = x.shape[0]
+    H, E = cfg.hidden, cfg.n_experts
+    _check(lib().moe_forward_noalloc(
+        ctypes.byref(cfg), T, _ptr(x, _act_dtype(cfg), (T, H), "x"),
+        _ptr(w_router, _act_dtype(cfg), (E, H), "w_router"),
+        _ptr(router_bias, torch.float32, (E,), "router_bias", optional=True),
+        _ptr(score_bias, torch.float32, (E,), "score_bias", optional=True), ctypes.byref(weights),
+        _ptr(y, _out_dtype(cfg), (T, H), "y"),
+        _ptr(logits_out, torch.float32, (T, E), "logits_out", optional=True),
+        _ptr(topk_ids_out, torch.int32, (T, cfg.top_k), "topk_ids_out", optional=True),
+        _stream(stream)), "moe_forward_noalloc")
 
 
 def moe_expert_load(cfg, topk_ids, load, stream=None):

@@ -664,6 +664,99 @@ bool weights_ok(const moe_config* c, const moe_weights* w) {
     return true;
 }
 
+// ---- the whole layer -----------------------------------------------------------
+
+// Argument checks of moe_forward and moe_forward_noalloc (the workspace aside).
+int check_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const moe_weights* weights,
+                  const void* y, const float* logits_out, const int32_t* topk_ids_out) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (T < 0 || T > INT32_MAX / 16) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !y || !weights_ok(cfg, weights)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(y) || (logits_out && !aligned16(logits_out)) ||
+        (topk_ids_out && !aligned16(topk_ids_out)))
+        return MOE_ERR_MISALIGNED;
+    if (!offsets_fit(cfg, T, false)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// Router GEMM, route, dispatch, experts, combine on `stream`, with workspace
+// `ws` (already checked). With `side_ok` the shared expert runs beside the
+// routed path on the side stream where that pays (overlap_shared); without
+// it, on `stream` after the routed experts, with the same kernels.
+int forward_body(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* router_bias,
+                 const float* score_bias, const moe_weights* weights, void* y, float* logits_out,
+                 int32_t* topk_ids_out, void* ws, hipStream_t stream, bool side_ok) {
+    const Layout L = layout(cfg, T);
+    float* logits = logits_out ? logits_out : at<float>(ws, L.logits);
+    int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+    float* w = at<float>(ws, L.w);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* inv = at<int32_t>(ws, L.inv);
+    void* rows = at<void>(ws, L.rows);
+    void* shared_out = cfg->shared_inter > 0 ? at<void>(ws, L.shared_out) : nullptr;
+    // At decode shapes the shared expert (which needs only x) starts first,
+    // on the side stream, and runs beside the routing kernels and the routed
+    // experts' grouped GEMMs (measured on the EP8 decode share: 0.917 ->
+    // 0.892 ms per layer).
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    SideStream* side = nullptr;
+    const bool overlap = side_ok && overlap_shared(cfg, T);
+    const bool late = shared_down_late(cfg, T);
+    hipError_t e = do_quant_x(cfg, T, x, ws, stream);
+    if (e == hipSuccess && overlap) e = fork_shared(cfg, T, x, weights, shared_out, ws, stream, late, &side);
+    LateSharedDown ld{side, cfg, T, x, weights, shared_out, ws, false};
+    if (e == hipSuccess) e = do_router_gemm(cfg, T, x, w_router, router_bias, logits, ws, stream);
+    if (e == hipSuccess) e = do_route(cfg, T, logits, score_bias, ids, w, stream);
+    if (e == hipSuccess)
+        e = do_dispatch(cfg, T, ids, at<int32_t>(ws, L.raw), at<int32_t>(ws, L.counts), offsets, perm, inv, ws,
+                        stream);
+    if (e == hipSuccess)
+        e = do_routed_ffn(cfg, T, x, perm, offsets, weights, rows, ws, stream, side && late ? &ld : nullptr);
+    if (side) {
+        // always rejoin the side stream
+        hipError_t j = late ? close_late_fork(ld) : hipSuccess;
+        if (j == hipSuccess) j = join_shared(side, stream);
+        if (e == hipSuccess) e = j;
+    } else if (e == hipSuccess && shared_out) {
+        e = do_shared_ffn(cfg, T, x, weights, shared_out, ws, stream);
+    }
+    if (e == hipSuccess) e = do_combine(cfg, T, rows, inv, w, shared_out, y, stream);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// ---- the workspace of moe_forward_noalloc ---------------------------------------
+// A device array of the library's own, one copy per GPU, held until the
+// process ends. In host code `scratch` names a host-side stand-in, not the
+// device memory: its device address is looked up once per device (with that
+// device current) by hipGetSymbolAddress, and only that address is ever
+// passed on. The layer writes every workspace region before reading it, so
+// nothing in it has to start at zero.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -764,53 +857,25 @@ int moe_combine(const moe_config* cfg, int64_t T, const void* out_rows, const in
 int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* router_bias,
                 const float* score_bias, const moe_weights* weights, void* y, float* logits_out,
                 int32_t* topk_ids_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-    int st = validate(cfg);
-    if (st) return st;
-    if (T < 0 || T > INT32_MAX / 16) return MOE_ERR_INVALID_ARG;
-    if (T == 0) return MOE_OK;
-    if (!x || !w_router || !y || !weights_ok(cfg, weights)) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(w_router) || !aligned16(y) || (logits_out && !aligned16(logits_out)) ||
-        (topk_ids_out && !aligned16(topk_ids_out)))
-        return MOE_ERR_MISALIGNED;
-    if (!offsets_fit(cfg, T, false)) return MOE_ERR_UNSUPPORTED;
+    int st = check_forward(cfg, T, x, w_router, weights, y, logits_out, topk_ids_out);
+    if (st || T == 0) return st;
     if ((st = check_ws(cfg, T, ws, ws_bytes))) return st;
-    const Layout L = layout(cfg, T);
-    float* logits = logits_out ? logits_out : at<float>(ws, L.logits);
-    int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
-    float* w = at<float>(ws, L.w);
-    int32_t* offsets = at<int32_t>(ws, L.offsets);
-    int32_t* perm = at<int32_t>(ws, L.perm);
-    int32_t* inv = at<int32_t>(ws, L.inv);
-    void* rows = at<void>(ws, L.rows);
-    void* shared_out = cfg->shared_inter > 0 ? at<void>(ws, L.shared_out) : nullptr;
-    // At decode shapes the shared expert (which needs only x) starts first,
-    // on the side stream, and runs beside the routing kernels and the routed
-    // experts' grouped GEMMs (measured on the EP8 decode share: 0.917 ->
-    // 0.892 ms per layer).
-    std::lock_guard<std::mutex> lk(g_side_mu);
-    SideStream* side = nullptr;
-    const bool overlap = overlap_shared(cfg, T);
-    const bool late = shared_down_late(cfg, T);
-    hipError_t e = do_quant_x(cfg, T, x, ws, stream);
-    if (e == hipSuccess && overlap) e = fork_shared(cfg, T, x, weights, shared_out, ws, stream, late, &side);
-    LateSharedDown ld{side, cfg, T, x, weights, shared_out, ws, false};
-    if (e == hipSuccess) e = do_router_gemm(cfg, T, x, w_router, router_bias, logits, ws, stream);
-    if (e == hipSuccess) e = do_route(cfg, T, logits, score_bias, ids, w, stream);
-    if (e == hipSuccess)
-        e = do_dispatch(cfg, T, ids, at<int32_t>(ws, L.raw), at<int32_t>(ws, L.counts), offsets, perm, inv, ws,
-                        stream);
-    if (e == hipSuccess)
-        e = do_routed_ffn(cfg, T, x, perm, offsets, weights, rows, ws, stream, side && late ? &ld : nullptr);
-    if (side) {
-        // always rejoin the side stream
-        hipError_t j = late ? close_late_fork(ld) : hipSuccess;
-        if (j == hipSuccess) j = join_shared(side, stream);
-        if (e == hipSuccess) e = j;
-    } else if (e == hipSuccess && shared_out) {
-        e = do_shared_ffn(cfg, T, x, weights, shared_out, ws, stream);
-    }
-    if (e == hipSuccess) e = do_combine(cfg, T, rows, inv, w, shared_out, y, stream);
-    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return forward_body(cfg, T, x, w_router, router_bias, score_bias, weights, y, logits_out, topk_ids_out, ws,
+                        stream, true);
+}
+
+int moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                        const float* router_bias, const float* score_bias, const moe_weights* weights, void* y,
+                        float* logits_out, int32_t* topk_ids_out, hipStream_t stream) {
+    int st = check_forward(cfg, T, x, w_router, weights, y, logits_out, topk_ids_out);
+    if (st || T == 0) return st;
+    if (layout(cfg, T).total > kScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return MOE_ERR_HIP;
+    // the shared expert runs on `stream` itself: no side stream or event is
+    // created (the kernels are those moe_forward picks, so results are equal)
+    return forward_body(cfg, T, x, w_router, router_bias, score_bias, weights, y, logits_out, topk_ids_out, ws,
+                        stream, false);
 }
 
 int moe_quantize_fp8(const moe_config* cfg, int64_t rows, const void* x, uint8_t* q, float* scale,

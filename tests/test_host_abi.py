@@ -191,6 +191,27 @@ def test_operands_past_4_gib_are_refused():
         assert st == (B.ERR_WORKSPACE_TOO_SMALL if ok else B.ERR_UNSUPPORTED)
 
 
+def test_noalloc_forward_rejects_before_launch():
+    """moe_forward_noalloc checks its arguments like moe_forward and refuses a
+    batch whose workspace exceeds its scratch array, before any HIP call."""
+    L = moe.lib()
+    c = _good()
+    cp = ctypes.byref(c)
+    W = B.Weights()
+    W.w13 = W.w2 = W.shared_w13 = W.shared_w2 = FAKE
+    assert L.moe_forward_noalloc(cp, 0, None, None, None, None, None, None, None, None, None) == B.OK
+    assert moe.workspace_bytes(c, 340) > moe.NOALLOC_SCRATCH_BYTES >= moe.workspace_bytes(c, 339)
+    assert L.moe_forward_noalloc(cp, 340, FAKE, FAKE, None, None, ctypes.byref(W), FAKE, None, None, None) == \
+        B.ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_forward_noalloc(cp, 4, FAKE + 4, FAKE, None, None, ctypes.byref(W), FAKE, None, None, None) == \
+        B.ERR_MISALIGNED
+    assert L.moe_forward_noalloc(cp, 4, None, FAKE, None, None, ctypes.byref(W), FAKE, None, None, None) == \
+        B.ERR_INVALID_ARG
+    bad = _good(n_group=7)
+    assert L.moe_forward_noalloc(ctypes.byref(bad), 4, FAKE, FAKE, None, None, ctypes.byref(W), FAKE, None, None,
+                                 None) == B.ERR_INVALID_ARG
+
+
 def test_binding_requires_gpu_tensors():
     import torch
     c = moe.make_config(512, 8, 2, 512, dtype="f32")
