@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-packed", action="store_true",
+                    help="bf16: run without the prepacked weight copy (the 256 x 256 tiles then read the "
+                         "canonical weights through LDS)")
     ap.add_argument("--graph", action="store_true",
                     help="capture the timed steps in one HIP graph and replay it (no launch gaps)")
     ap.add_argument("--diag-steps", type=int, default=10,
@@ -57,7 +60,7 @@ def parse():
 
 
 # Kernel sources whose code a stored traffic measurement belongs to.
-KERNEL_SOURCES = {"bf16": ["gemm.hip", "gemm_big.hip", "gemm_cores.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
+KERNEL_SOURCES = {"bf16": ["gemm.hip", "gemm_big.hip", "gemm_pf.hip", "gemm_cores.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
                   "f32": ["gemm.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
                   "fp8": ["gemm_fp8.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"],
                   "mxfp4": ["gemm_mx.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"]}
@@ -263,6 +266,12 @@ def measure(name, a, peaks=None):
     cfg = moe.config_from_workload(w, out_dtype=a.out_dtype)
     W = moe.make_weights(cfg, inp["w13"], inp["w2"], inp["shared_w13"], inp["shared_w2"], inp.get("w13_scale"),
                          inp.get("w2_scale"), inp.get("shared_w13_scale"), inp.get("shared_w2_scale"))
+    packed = None
+    if w["dtype"] == "bf16" and not a.no_packed:
+        # the prepacked copy (once, untimed): the layer's 256 x 256 tiles
+        # stream their weights from it
+        packed = moe.moe_prepack_weights(cfg, W)
+        W = moe.make_weights(cfg, inp["w13"], inp["w2"], inp["shared_w13"], inp["shared_w2"], packed=packed)
     ws = moe.workspace(cfg, T)
     y = torch.empty(T, w["hidden"], dtype=torch.bfloat16 if a.out_dtype == "bf16" else torch.float32,
                     device="cuda")
@@ -351,7 +360,8 @@ def measure(name, a, peaks=None):
         roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": peak_mfma, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = stored_traffic(dom, name, w["dtype"])
-    family = {"fp8": "gemm_fp8_kernel", "mxfp4": "gemm_mx_kernel"}.get(w["dtype"], "gemm_kernel / gemm_big_kernel")
+    family = {"fp8": "gemm_fp8_kernel", "mxfp4": "gemm_mx_kernel"}.get(
+        w["dtype"], "gemm_kernel / gemm_pf_kernel" if packed is not None else "gemm_kernel / gemm_big_kernel")
     roof["kernel"] = f"{family} ({dom})"
     roof["kernel_ms"] = t_dom * 1e3
     roof["kernel_launches_timed"] = dom_n
@@ -393,11 +403,12 @@ def measure(name, a, peaks=None):
         "dtype": w["dtype"],
         "config": {"workload": name, "tokens": T, "hidden": w["hidden"], "experts": w["n_experts"],
                    "local_experts": [w["expert_begin"], w["expert_end"]], "top_k": w["top_k"],
-                   "inter": w["inter"], "shared_inter": w["shared_inter"], "out_dtype": a.out_dtype},
+                   "inter": w["inter"], "shared_inter": w["shared_inter"], "out_dtype": a.out_dtype,
+                   "packed_weights": packed is not None},
         "roofline": roof, "grouped_gemm": grouped, "stage_ms": stage_ms, "step_ms": step_pct,
         "rows": int(counts.sum()), "max_rows_per_expert": int(counts.max()), "expert_load": expert_load,
     }
-    del W, ws, y
+    del W, ws, y, packed
     return res, (w, inp)
 
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 enum moe_status {
@@ -128,7 +128,13 @@ typedef struct moe_config {
  *            MXFP4: E8M0 bytes [E_l, 2I, H/32], [E_l, H, I/32] and
  *            [2 I_s, H/32], [H, I_s/32] (8-byte aligned); NULL otherwise.
  * MXFP4 weight rows are packed two E2M1 codes per byte, element 2i in the low
- * nibble: w13 [E_l, 2I, H/2] bytes, w2 [E_l, H, I/2] bytes. */
+ * nibble: w13 [E_l, 2I, H/2] bytes, w2 [E_l, H, I/2] bytes.
+ *  packed    BF16 only, optional (NULL: none): the buffer moe_prepack_weights
+ *            filled from these same weights. With it, batches whose gate/up
+ *            GEMMs take the 256 x 256 compute-bound tiles (hundreds of rows
+ *            per expert: prefill shapes) stream the gate/up weights from it
+ *            straight into registers; every other GEMM still reads the
+ *            canonical arrays, which stay required. */
 typedef struct moe_weights {
     const void* w13;
     const void* w2;
@@ -138,6 +144,7 @@ typedef struct moe_weights {
     const void* shared_w2;
     const void* shared_w13_scale;
     const void* shared_w2_scale;
+    const void* packed;
 } moe_weights;
 
 int moe_abi_version(void);
@@ -152,6 +159,35 @@ int moe_validate_config(const moe_config* cfg);
 /* Bytes of workspace that moe_forward (and each stage call) needs for up to
  * max_tokens tokens. Written to *bytes. */
 int moe_workspace_bytes(const moe_config* cfg, int64_t max_tokens, size_t* bytes);
+
+/* Prepacked expert weights for the compute-bound grouped GEMM (BF16 layers).
+ * The expert FFN is three matrices per expert, gate, up and down (infra guide
+ * "Data parallelism and expert parallelism", section 2.1); at prefill shapes
+ * its grouped GEMM is bound by the matrix cores (Perplexity, "Roofline >
+ * GroupGEMM"), and the 256 x 256 gate/up tiles then stream each weight panel
+ * from HBM straight into registers, as MFMA operand fragments in the order
+ * they are consumed. The packed buffer holds, 256-byte aligned and in this
+ * order: the routed w13 [E_l] blocks and (when shared_inter > 0) the shared
+ * w13 block, each the size of its canonical array. (The down projection is
+ * read in canonical layout by every tile shape.)
+ * A block of an [2I, K] gate/up weight is a sequence of 64-row panels, each
+ * of K/16 steps of 2 KB: panel p holds gate rows 32p..32p+31 (half 0) and the
+ * up rows I + 32p..I + 32p + 31 of the same h columns (half 1). Element
+ * (row n, column k) of half h, with n' its index within the half, sits at
+ * byte ((p * K/16 + k/16) * 2 + h) * 1024 + (n' + 32 * ((k/8) % 2)) * 16
+ * + (k % 8) * 2 of the block: one lane's 8 consecutive K values per 16 bytes,
+ * a wavefront's two 32 x 16 fragments of a K step in 2 KB of consecutive
+ * memory.
+ *
+ * moe_packed_weights_bytes: the packed buffer's size for cfg (BF16 only;
+ * other dtypes return MOE_ERR_UNSUPPORTED). Host only.
+ * moe_prepack_weights: fills `packed` (device, 256-byte aligned, at least
+ * packed_bytes = moe_packed_weights_bytes) from the canonical weights
+ * (w13 and, with a shared expert, shared_w13; device). Asynchronous on
+ * `stream`; run once, before the weights are used. */
+int moe_packed_weights_bytes(const moe_config* cfg, size_t* bytes);
+int moe_prepack_weights(const moe_config* cfg, const moe_weights* canonical, void* packed, size_t packed_bytes,
+                        hipStream_t stream);
 
 /* Router GEMM: logits[T, E] (fp32) = x[T, H] . w_router[E, H]^T + router_bias.
  * x and w_router are fp32 (F32) or bf16 (BF16, FP8, MXFP4): inputs of the activation
@@ -241,7 +277,14 @@ int moe_quantize_fp8(const moe_config* cfg, int64_t rows, const void* x, uint8_t
 int moe_quantize_mx(const moe_config* cfg, int64_t rows, const void* x, uint8_t* q, uint8_t* scale,
                     hipStream_t stream);
 
-/* The whole layer: router GEMM, route, dispatch, experts, combine.
+/* The whole layer: router GEMM, route, dispatch, experts, combine, in the
+ * order of the four steps (Ultralytics glossary "Expert Parallelism", section
+ * "How tokens move between GPUs": route, dispatch, compute, combine; infra
+ * guide "Data parallelism and expert parallelism", section 3.1), with the
+ * shared expert added to every token (Perplexity, "Expert parallelism"). One
+ * GPU holds the experts [expert_begin, expert_end): dispatch and combine are
+ * local permutations, and y is that share's partial output plus the shared
+ * expert's.
  *  x [T, H], w_router [E, H] (activation type; bf16 for FP8 and MXFP4), router_bias [E]
  *  and score_bias [E] fp32 or NULL, weights as above; y [T, H] out.
  *  logits_out [T, E] fp32 and topk_ids_out [T, k] int32, if not NULL, receive

@@ -14,7 +14,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_MISALIGNED, ERR_HIP, ERR_ABI_MISMATCH = \
     0, -1, -2, -3, -4, -5, -6
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
@@ -43,7 +43,7 @@ class Config(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("w13", "w2", "w13_scale", "w2_scale", "shared_w13", "shared_w2",
-                 "shared_w13_scale", "shared_w2_scale")]
+                 "shared_w13_scale", "shared_w2_scale", "packed")]
 
 
 _lib = None
@@ -71,6 +71,8 @@ def lib():
             "moe_combine": (ctypes.c_int, [cfgp, i64, vp, i32p, fp, vp, vp, vp]),
             "moe_forward": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, wp, vp, fp, i32p, vp, ctypes.c_size_t, vp]),
             "moe_forward_noalloc": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, wp, vp, fp, i32p, vp]),
+            "moe_packed_weights_bytes": (ctypes.c_int, [cfgp, ctypes.POINTER(ctypes.c_size_t)]),
+            "moe_prepack_weights": (ctypes.c_int, [cfgp, wp, vp, ctypes.c_size_t, vp]),
             "moe_quantize_fp8": (ctypes.c_int, [cfgp, i64, vp, vp, fp, vp]),
             "moe_quantize_mx": (ctypes.c_int, [cfgp, i64, vp, vp, vp, vp]),
             "moe_expert_load": (ctypes.c_int, [cfgp, i64, vp, vp, vp]),
@@ -199,8 +201,9 @@ def _weight_dtype(cfg):
 
 
 def make_weights(cfg, w13, w2, shared_w13=None, shared_w2=None, w13_scale=None, w2_scale=None,
-                 shared_w13_scale=None, shared_w2_scale=None):
-    """Pack weight tensor pointers (the tensors must outlive the calls)."""
+                 shared_w13_scale=None, shared_w2_scale=None, packed=None):
+    """Pack weight tensor pointers (the tensors must outlive the calls).
+    `packed`: the uint8 device buffer moe_prepack_weights filled (bf16), or None."""
     El, H, I, Is = cfg.n_local, cfg.hidden, cfg.inter, cfg.shared_inter
     wd = _weight_dtype(cfg)
     W = Weights()
@@ -224,8 +227,27 @@ def make_weights(cfg, w13, w2, shared_w13=None, shared_w2=None, w13_scale=None, 
         if Is > 0:
             W.shared_w13_scale = _ptr(shared_w13_scale, f32, (2 * Is // 128, H // 128), "shared_w13_scale")
             W.shared_w2_scale = _ptr(shared_w2_scale, f32, (H // 128, Is // 128), "shared_w2_scale")
-    W._keep = (w13, w2, shared_w13, shared_w2, w13_scale, w2_scale, shared_w13_scale, shared_w2_scale)
+    if packed is not None:
+        W.packed = _ptr(packed, torch.uint8, None, "packed")
+    W._keep = (w13, w2, shared_w13, shared_w2, w13_scale, w2_scale, shared_w13_scale, shared_w2_scale, packed)
     return W
+
+
+def packed_weights_bytes(cfg):
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_packed_weights_bytes(ctypes.byref(cfg), ctypes.byref(n)), "moe_packed_weights_bytes")
+    return n.value
+
+
+def moe_prepack_weights(cfg, weights, packed=None, stream=None):
+    """Fills (or allocates, when `packed` is None) the packed weight buffer
+    from the canonical weights of `weights` (a Weights record); returns it."""
+    n = packed_weights_bytes(cfg)
+    if packed is None:
+        packed = torch.empty(n, dtype=torch.uint8, device="cuda")
+    _check(lib().moe_prepack_weights(ctypes.byref(cfg), ctypes.byref(weights), _ptr(packed, torch.uint8, None, "packed"),
+                                     packed.numel(), _stream(stream)), "moe_prepack_weights")
+    return packed
 
 
 # ---------------------------------------------------------------------------

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "gemm.hip", "gemm_big.hip", "gemm_fp8.hip", "gemm_mx.hip", "combine.hip", "load_stats.hip", "peak.hip", "gemm_cores.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "gemm.hip", "gemm_big.hip", "gemm_pf.hip", "gemm_fp8.hip", "gemm_mx.hip", "combine.hip", "load_stats.hip", "peak.hip", "gemm_cores.hip"]
 EXTRA = {"route.hip": ["-ffp-contract=off"]}
 
 

@@ -600,6 +600,7 @@ hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_
 
 hipError_t launch_gemm(Elem e, Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     if (p.grid == 0) return hipSuccess;
+    if (p.big == 2) return e == Elem::BF16 ? launch_gemm_pf(epi, a, p, s) : hipErrorInvalidValue;
     if (p.big) return e == Elem::BF16 ? launch_gemm_big(epi, a, p, s) : hipErrorInvalidValue;
     if (e == Elem::BF16)
         return epi == Epi::SWIGLU ? launch_bm<Elem::BF16, Epi::SWIGLU>(a, p, s) : launch_bm<Elem::BF16, Epi::PLAIN>(a, p, s);

@@ -1,0 +1,456 @@
+// K5 / K6 at compute-bound shapes (bf16) on prepacked weights: grouped GEMM
+// with 256 x 256 tiles, the activation tile staged through a four-slot LDS
+// ring and the weights streamed from HBM straight into registers.
+//
+// What it computes is that of gemm.hip (Perplexity "Lower latency and higher
+// throughput with multi-node DeepSeek deployment", section "Roofline >
+// GroupGEMM": per group, rows x weight^T; SWIGLU epilogue h = silu(gate) * up,
+// infra guide "Data parallelism and expert parallelism", section 2.1). At
+// prefill shapes (hundreds of rows per expert) the product is bound by the
+// matrix cores, and what keeps them busy is hiding every load behind MFMAs:
+//
+//  * a workgroup of 4 wavefronts computes 256 rows x 4 weight panels of 64
+//    rows (SWIGLU: 32 gate rows + the 32 up rows of the same h columns;
+//    PLAIN: 64 consecutive rows); wavefront w owns panel w and all 256 rows,
+//    as 8 x 2 fragments of v_mfma_f32_32x32x16_bf16 (256 accumulators, held
+//    in the accumulation registers: one wavefront per SIMD);
+//  * the weights come from the prepacked layout (moe_prepack_weights), in
+//    which one wavefront's operand fragments of a 16-deep K step are 2 KB of
+//    consecutive memory: two fully coalesced 16-byte loads per lane, issued
+//    three K-stages (192 K) ahead into a four-stage register ring, never
+//    through LDS;
+//  * the activation rows (gathered through the dispatch permutation) go
+//    HBM/L2 -> LDS by global_load_lds_dwordx4, K = 64 per stage (each row's
+//    128 bytes one whole cache line), into a ring of four 32 KB slots, four
+//    stages ahead (a slot is refilled as soon as the barrier after its last
+//    read has passed);
+//  * one barrier per stage, placed mid-stage, that waits only for the loads
+//    the next stage needs (vmcnt counts outstanding loads in issue order), so
+//    loads issued later stay in flight across it; the MFMAs of the stage's
+//    last two K steps run while the next stage's first fragments are read;
+//  * 16-byte granule q of LDS row r sits at q ^ ((r >> 1) & 7): the fragment
+//    reads (32 rows x one granule per lane half) are free of bank conflicts;
+//  * a group's rows are split evenly over its m-tiles; 32-row blocks past the
+//    tile's rows skip their MFMAs;
+//  * the epilogue stages the tile in the idle LDS ring and writes whole
+//    16-byte pieces of rows.
+#include <utility>
+
+#include "gemm_tile.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBM = 256;                 // rows per tile
+constexpr int kNW = 4;                   // wavefronts (one weight panel each)
+constexpr int kNT = kNW * 64;            // threads
+constexpr int kKB = 64;                  // K per stage
+constexpr int kRowB = kKB * 2;           // LDS bytes per row per stage
+constexpr int kGran = kRowB / 16;        // 16-byte granules per row
+constexpr int kSlots = 4;                // LDS ring
+constexpr int kSlotB = kBM * kRowB;      // 32 KB
+constexpr int kALoads = kBM * kGran / kNT;       // direct loads per thread per stage (8)
+constexpr int kRowsPerLoad = 64 / kGran;         // rows one direct load instruction fills (8)
+constexpr int kKSteps = kKB / 16;                // MFMA K steps per stage (4)
+constexpr int kFragB = 1024;                     // bytes of one 32 x 16 operand fragment
+constexpr int kStepB = 2 * kFragB;               // packed bytes of a panel per K step
+
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ bf16x8 frag(const vec16& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ float silu_mul_pf(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]).
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+template <Epi EPI>
+__global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles) {
+    // The LDS ring as four separate arrays, each indexed only by a constant
+    // slot number: the compiler then knows that a fragment read of one slot
+    // cannot alias a direct load into another, and does not make the read
+    // wait for every direct load in flight.
+    __shared__ __attribute__((aligned(16))) unsigned char s_a0[kSlotB], s_a1[kSlotB], s_a2[kSlotB], s_a3[kSlotB];
+    auto slot = [&](auto u_c) __attribute__((always_inline)) -> unsigned char* {
+        constexpr int U = decltype(u_c)::value % kSlots;
+        return U == 0 ? s_a0 : U == 1 ? s_a1 : U == 2 ? s_a2 : s_a3;
+    };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    Tile tl;
+    if (!find_tile(a, n_tiles, kBM, tl, /*balanced=*/true)) return;
+    const int g = tl.g, nt = tl.nt;
+    const bool shared = tl.shared;
+    const int row0 = tl.row0, m0 = tl.m0, rows = tl.rows;
+    const int K = a.K;
+    const int nkb = K / kKB;
+    const int last = nkb - 1;
+    const int nrb = (rows + 31) >> 5;                 // 32-row blocks with data (uniform)
+
+    // ---- activation rows: load j of wavefront w fills rows (4 j + w) * 8 +
+    // lane / 8 of the slot, granule position lane % 8, with the granule the
+    // swizzle puts there. The gathered source rows are looked up with all
+    // eight permutation loads in flight together. ------------------------------
+    const int lrow = lane / kGran;
+    const unsigned char* Ag = static_cast<const unsigned char*>(shared ? a.A_shared : a.A);
+    int rsl[kALoads];
+    uint32_t src[kALoads];
+#pragma unroll
+    for (int j = 0; j < kALoads; ++j) {
+        const int rs = (kNW * j + wave) * kRowsPerLoad + lrow;
+        rsl[j] = rs;
+        src[j] = static_cast<uint32_t>(rs < rows ? rs : rows - 1);   // rows past the end: a valid row, unused
+    }
+    if (shared) {
+#pragma unroll
+        for (int j = 0; j < kALoads; ++j) src[j] += m0;
+    } else if (a.gather) {
+        int pv[kALoads];
+#pragma unroll
+        for (int j = 0; j < kALoads; ++j) pv[j] = a.perm[row0 + m0 + static_cast<int>(src[j])];
+#pragma unroll
+        for (int j = 0; j < kALoads; ++j) src[j] = static_cast<uint32_t>(pv[j] / a.topk);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kALoads; ++j) src[j] += row0 + m0;
+    }
+    uint32_t aoff[kALoads];
+#pragma unroll
+    for (int j = 0; j < kALoads; ++j)
+        aoff[j] = src[j] * static_cast<uint32_t>(K * 2) + (((lane % kGran) ^ swz(rsl[j])) * 16);
+
+    // ---- weights: this wavefront's panel of the packed layout ----------------
+    // A panel past the last one (N not a multiple of the tile) reads the last
+    // panel; its results are dropped.
+    const int n_panels = EPI == Epi::SWIGLU ? a.inter / 32 : a.N / 64;
+    int panel = nt * kNW + wave;
+    panel = panel < n_panels ? panel : n_panels - 1;
+    const unsigned char* Bw = static_cast<const unsigned char*>(shared ? a.B_shared : a.B) +
+                              (shared ? int64_t{0} : static_cast<int64_t>(g) * a.b_stride * 2) +
+                              static_cast<int64_t>(panel) * (K / 16) * kStepB;
+    const uint32_t boff = static_cast<uint32_t>(lane) * 16;
+
+    // A(kb) -> slot kb % 4 (kb past the end: the last stage again, into a
+    // slot nobody reads any more)
+    auto issue_a = [&](auto u_c, int kb) __attribute__((always_inline)) {
+        const int kc = kb < last ? kb : last;
+        unsigned char* sa = slot(u_c);
+        const uint32_t ko = static_cast<uint32_t>(kc) * kRowB;
+#pragma unroll
+        for (int j = 0; j < kALoads; ++j)
+            load_lds16(Ag + aoff[j] + ko, sa + (kNW * j + wave) * kRowsPerLoad * kRowB);
+    };
+    // B register ring: four stages x 4 K steps x (gate/low, up/high) halves;
+    // B(kb) -> ring slot kb % 4.
+    vec16 br[4][kKSteps][2];
+    auto issue_b = [&](auto u_c, int kb) __attribute__((always_inline)) {
+        constexpr int S = decltype(u_c)::value % 4;
+        const int kc = kb < last ? kb : last;
+        const unsigned char* p = Bw + static_cast<int64_t>(kc) * kKSteps * kStepB;
+#pragma unroll
+        for (int t = 0; t < kKSteps; ++t) {
+            br[S][t][0] = ld16(p + t * kStepB + boff);
+            br[S][t][1] = ld16(p + t * kStepB + kFragB + boff);
+        }
+    };
+    // One load of A(kb) or B(kb) (load j of the stage's eight), for issuing
+    // the loads one at a time between MFMAs.
+    auto issue_a_one = [&](auto u_c, auto j_c, int kb) __attribute__((always_inline)) {
+        constexpr int J = decltype(j_c)::value;
+        const int kc = kb < last ? kb : last;
+        load_lds16(Ag + aoff[J] + static_cast<uint32_t>(kc) * kRowB,
+                   slot(u_c) + (kNW * J + wave) * kRowsPerLoad * kRowB);
+    };
+    auto issue_b_one = [&](auto u_c, auto j_c, int kb) __attribute__((always_inline)) {
+        constexpr int S = decltype(u_c)::value % 4;
+        constexpr int J = decltype(j_c)::value;
+        const int kc = kb < last ? kb : last;
+        const unsigned char* p = Bw + static_cast<int64_t>(kc) * kKSteps * kStepB;
+        br[S][J / 2][J % 2] = ld16(p + (J / 2) * kStepB + (J % 2) * kFragB + boff);
+    };
+
+    // ---- fragment reads: lane l reads row l % 32 of a 32-row block, granule
+    // 2 t + l / 32 of K step t ------------------------------------------------
+    const int fr = lane & 31;
+    int f_off[kKSteps];
+#pragma unroll
+    for (int t = 0; t < kKSteps; ++t) f_off[t] = fr * kRowB + (((2 * t + (lane >> 5)) ^ swz(fr)) * 16);
+
+    f32x16 acc[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = f32x16{};
+
+    // A fragments of K step t in buffer t % 2, all 8 blocks read whatever the
+    // tile's height (rows past its end hold copies of its last row), so
+    // that every path through the loop has the same LDS reads in flight and
+    // the compiler waits for exactly those each MFMA needs; only the MFMAs
+    // of blocks without rows are skipped (a branch on a uniform value).
+    bf16x8 af[2][8];
+    auto read = [&](auto u_c, auto t_c) __attribute__((always_inline)) {
+        constexpr int T = decltype(t_c)::value;
+        const unsigned char* st = slot(u_c) + f_off[T];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) af[T % 2][i] = frag(ld16(st + i * 32 * kRowB));
+    };
+    // MFMAs of K step t for row blocks [I0, I0 + 4); after each block's pair,
+    // ld(i) issues one load (unconditionally). With one wavefront per SIMD a
+    // load holds up the wavefront's issue while its addresses are taken in;
+    // behind an MFMA that time is hidden by the MFMA's own 32 cycles.
+    auto mfma = [&](auto u_c, auto t_c, auto i0_c, auto ld) __attribute__((always_inline)) {
+        constexpr int S = decltype(u_c)::value % 4;
+        constexpr int T = decltype(t_c)::value;
+        constexpr int I0 = decltype(i0_c)::value;
+        auto block = [&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            if (__builtin_expect(i < nrb, 1)) {          // full tiles: straight-line code
+                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[T % 2][i], frag(br[S][T][0]), acc[i][0], 0, 0, 0);
+                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[T % 2][i], frag(br[S][T][1]), acc[i][1], 0, 0, 0);
+            }
+            ld(i_c);
+        };
+        block(std::integral_constant<int, I0>{});
+        block(std::integral_constant<int, I0 + 1>{});
+        block(std::integral_constant<int, I0 + 2>{});
+        block(std::integral_constant<int, I0 + 3>{});
+    };
+    auto none = [](auto) {};
+    // Wait until at most VM loads of this thread are outstanding (and, with
+    // LGKM, its LDS reads are done), then, with BAR, a bare barrier (no
+    // fence: the fills are waited for explicitly). The empty asm statements
+    // keep the compiler from moving memory accesses across it, the scheduling
+    // barriers keep MFMAs on their side of it.
+    auto wait = [&](auto vm_c, auto bar_c) __attribute__((always_inline)) {
+        constexpr bool BAR = decltype(bar_c)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(decltype(vm_c)::value, BAR ? 0 : 15));
+        asm volatile("" ::: "memory");
+        if constexpr (BAR) {
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    using Yes = std::true_type;
+    using No = std::false_type;
+    constexpr int kGroup = 2 * kALoads;                             // loads of one stage (A and B: 8 each)
+
+    // ---- pipeline -----------------------------------------------------------
+    // Iteration j issues B(j + 3), then, after its mid-stage barrier, A(j + 4);
+    // the prologue stands in for iterations -4..-1. Iteration j (stage j in
+    // LDS slot j % 4 and ring slot j % 4; K step 0's fragments already read):
+    //   wait for B(j)  [after it: A(j+1), B(j+1), A(j+2), B(j+2), A(j+3)]  vmcnt(40)
+    //   MFMAs of step 0 with the reads of step 1 between their halves, and
+    //   likewise steps 1 and 2;
+    //   (B(j+3), ring slot (j-1) % 4, last read by stage j-1, is issued
+    //   between the MFMAs of step 0)
+    //   wait for A(j+1) [after it: B(j+1), A(j+2), B(j+2), A(j+3), B(j+3)] vmcnt(40)
+    //   and this thread's LDS reads, then barrier: A(j+1) has landed for
+    //   every wavefront and nobody reads slot j % 4 any more;
+    //   MFMAs of step 3 with A(j+4) (slot j % 4) issued between them, and
+    //   the reads of step 0 of stage j+1.
+    // Loads past the last stage re-read it into free slots, so the wait
+    // counts hold to the end.
+    issue_a(C0{}, 0);
+    issue_b(C0{}, 0);
+    issue_a(C1{}, 1);
+    issue_b(C1{}, 1);
+    issue_a(C2{}, 2);
+    issue_b(C2{}, 2);
+    issue_a(C3{}, 3);
+    wait(std::integral_constant<int, 3 * kGroup>{}, Yes{});         // A(0) for every wavefront
+    read(C0{}, C0{});
+
+    // The fragment reads of the next K step sit between the two halves of a
+    // step's MFMAs, so that eight MFMAs cover their latency whatever wait the
+    // compiler puts before the next step's MFMAs (at a branch join it waits
+    // for every LDS read in flight). B(j + 3) is issued during K step 0 (its
+    // ring slot was last read by stage j - 1), A(j + 4) during K step 3,
+    // after the barrier that frees its LDS slot: one load per MFMA pair.
+    using L4 = std::integral_constant<int, 0>;
+    using H4 = std::integral_constant<int, 4>;
+    auto iteration = [&](auto u_c, int kb) __attribute__((always_inline)) {
+        constexpr int U = decltype(u_c)::value;
+        using N = std::integral_constant<int, (U + 1) % 4>;
+        using P = std::integral_constant<int, (U + 3) % 4>;
+        auto ldb = [&](auto j_c) __attribute__((always_inline)) { issue_b_one(P{}, j_c, kb + 3); };
+        auto lda = [&](auto j_c) __attribute__((always_inline)) { issue_a_one(u_c, j_c, kb + 4); };
+        // B(j): after it A(j+1), B(j+1), A(j+2), B(j+2), A(j+3)
+        wait(std::integral_constant<int, 5 * kALoads>{}, No{});
+        mfma(u_c, C0{}, L4{}, ldb);
+        read(u_c, C1{});
+        mfma(u_c, C0{}, H4{}, ldb);
+        mfma(u_c, C1{}, L4{}, none);
+        read(u_c, C2{});
+        mfma(u_c, C1{}, H4{}, none);
+        mfma(u_c, C2{}, L4{}, none);
+        read(u_c, C3{});
+        mfma(u_c, C2{}, H4{}, none);
+        // A(j+1) for every wavefront: after it B(j+1), A(j+2), B(j+2), A(j+3), B(j+3)
+        wait(std::integral_constant<int, 5 * kALoads>{}, Yes{});
+        mfma(u_c, C3{}, L4{}, lda);
+        read(N{}, C0{});
+        mfma(u_c, C3{}, H4{}, lda);
+    };
+    // Whole groups of four stages, no conditional code beyond the row-block
+    // checks; then the last zero to three stages.
+    int kb = 0;
+    for (; kb + 4 <= nkb; kb += 4) {
+        iteration(C0{}, kb);
+        iteration(C1{}, kb + 1);
+        iteration(C2{}, kb + 2);
+        iteration(C3{}, kb + 3);
+    }
+    if (kb < nkb) iteration(C0{}, kb);
+    if (kb + 1 < nkb) iteration(C1{}, kb + 1);
+    if (kb + 2 < nkb) iteration(C2{}, kb + 2);
+    // no direct-load write may outlive the loop: the epilogue reuses the ring
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __syncthreads();
+
+    // ---- epilogue: lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32)
+    // + e % 4 of each 32 x 32 fragment. Rows are staged 64 per LDS slot. ------
+    const int64_t crow0 = shared ? m0 : static_cast<int64_t>(row0) + m0;
+    unsigned char* Cb = static_cast<unsigned char*>(shared ? a.C_shared : a.C);
+    const int lc = lane & 31, lh = lane >> 5;
+    constexpr int TC = EPI == Epi::SWIGLU ? 32 * kNW : 64 * kNW;     // output columns of the tile
+    auto epilogue = [&](auto f32_out) __attribute__((always_inline)) {
+        constexpr bool F32 = decltype(f32_out)::value;
+        constexpr int EB = F32 ? 4 : 2;
+        constexpr int PC = F32 ? TC / 2 : TC;                         // columns per pass (<= 512 B a row)
+        constexpr int PRB = PC * EB;
+        constexpr int GPR = PRB / 16;
+        static_assert(64 * PRB <= kSlotB, "64 staged rows per slot");
+        auto pass = [&](auto pass_c) __attribute__((always_inline)) {
+            constexpr int P = decltype(pass_c)::value;
+            if constexpr (P > 0) __syncthreads();                     // the previous pass's stores are done
+            auto put = [&](auto i_c) __attribute__((always_inline)) {
+                constexpr int I = decltype(i_c)::value;
+                if (I < nrb) {
+                    unsigned char* sl = slot(std::integral_constant<int, I / 2>{});
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int r = (I % 2) * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);   // row within the slot
+                        unsigned char* row = sl + r * PRB;
+                        if constexpr (EPI == Epi::SWIGLU) {
+                            reinterpret_cast<uint16_t*>(row)[wave * 32 + lc] =
+                                f32_to_bf16_bits(silu_mul_pf(acc[I][0][e], acc[I][1][e]));
+                        } else {
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                const int col = wave * 64 + h * 32 - P * PC;   // the fragment's first column in the pass
+                                if (col >= 0 && col < PC) {                    // uniform
+                                    if constexpr (F32)
+                                        reinterpret_cast<float*>(row)[col + lc] = acc[I][h][e];
+                                    else
+                                        reinterpret_cast<uint16_t*>(row)[col + lc] = f32_to_bf16_bits(acc[I][h][e]);
+                                }
+                            }
+                        }
+                    }
+                }
+            };
+            put(std::integral_constant<int, 0>{});
+            put(std::integral_constant<int, 1>{});
+            put(std::integral_constant<int, 2>{});
+            put(std::integral_constant<int, 3>{});
+            put(std::integral_constant<int, 4>{});
+            put(std::integral_constant<int, 5>{});
+            put(std::integral_constant<int, 6>{});
+            put(std::integral_constant<int, 7>{});
+            __syncthreads();
+            // N and ldc are multiples of 8 (checked at launch), so a 16-byte
+            // piece lies wholly inside or wholly past the output's columns.
+            const int c0 = nt * TC + P * PC;
+            for (int q = tid; q < rows * GPR; q += kNT) {
+                const int r = q / GPR, gq = q % GPR;
+                const int col = c0 + gq * (16 / EB);
+                const unsigned char* sl = r < 64 ? s_a0 : r < 128 ? s_a1 : r < 192 ? s_a2 : s_a3;
+                if (col < a.N)
+                    st16(Cb + ((crow0 + r) * a.ldc + col) * EB, *reinterpret_cast<const vec16*>(sl + (r & 63) * PRB + gq * 16));
+            }
+        };
+        pass(std::integral_constant<int, 0>{});
+        if constexpr (F32) pass(std::integral_constant<int, 1>{});
+    };
+    if constexpr (EPI == Epi::PLAIN) {
+        if (a.out_f32) {
+            epilogue(std::true_type{});
+            return;
+        }
+    }
+    epilogue(std::false_type{});
+}
+
+template <Epi EPI>
+hipError_t launch_pf_epi(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_pf_kernel<EPI>), dim3(static_cast<unsigned>(p.grid)), dim3(kNT), 0, s, a, p.n_tiles);
+    return hipGetLastError();
+}
+
+// Packed layout: element (row n, column k) of an [N_B, K] weight, for the
+// panel p, half h and lane l holding it (see moe_prepack_weights), sits at
+// byte ((p * K/16 + k/16) * 2 + h) * 1024 + l * 16 + (k % 8) * 2, with
+// l = n_in_half + 32 * ((k / 8) % 2).
+__global__ __launch_bounds__(256) void prepack_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                      int64_t n_chunks, int K, int inter, int swiglu) {
+    // one thread per 16-byte packed chunk: (panel, k step, half, lane)
+    for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < n_chunks;
+         c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int l = static_cast<int>(c & 63);
+        const int h = static_cast<int>((c >> 6) & 1);
+        const int64_t ps = c >> 7;                   // panel * K/16 + k step
+        const int ksteps = K / 16;
+        const int64_t p = ps / ksteps;
+        const int s = static_cast<int>(ps - p * ksteps);
+        const int64_t n = swiglu ? (h ? inter : 0) + p * 32 + (l & 31) : p * 64 + h * 32 + (l & 31);
+        const int k = s * 16 + (l >> 5) * 8;
+        st16(dst + c * 8, ld16(src + n * K + k));
+    }
+}
+
+}  // namespace
+
+GemmPlan plan_gemm_pf(Epi epi, int64_t rows_upper, int n_groups, int N) {
+    GemmPlan p = plan_gemm_big(epi, rows_upper, n_groups, N);
+    p.nw = kNW;
+    p.big = 2;
+    return p;
+}
+
+hipError_t launch_gemm_pf(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+    if (p.grid == 0) return hipSuccess;
+    if (a.K % kKB != 0 || a.N % 8 != 0 || a.ldc % 8 != 0) return hipErrorInvalidValue;
+    if (epi == Epi::SWIGLU ? a.inter % 32 != 0 : a.N % 64 != 0) return hipErrorInvalidValue;
+    GemmArgs b = a;
+    b.ksplit = 1;
+    return epi == Epi::SWIGLU ? launch_pf_epi<Epi::SWIGLU>(b, p, s) : launch_pf_epi<Epi::PLAIN>(b, p, s);
+}
+
+hipError_t launch_prepack(const void* src, void* dst, int64_t n_experts, int n_rows, int K, int inter, bool swiglu,
+                          hipStream_t s) {
+    const int64_t per = static_cast<int64_t>(n_rows) * K / 8;      // 16-byte chunks per expert
+    for (int64_t e = 0; e < n_experts; ++e) {
+        const int64_t blocks = std::min<int64_t>((per + 255) / 256, 8192);
+        hipLaunchKernelGGL(prepack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(src) + e * n_rows * K,
+                           static_cast<uint16_t*>(dst) + e * n_rows * K, per, K, inter, swiglu ? 1 : 0);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+}  // namespace moe

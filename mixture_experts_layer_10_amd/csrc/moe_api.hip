@@ -140,6 +140,36 @@ Layout layout(const moe_config* c, int64_t T) {
     return L;
 }
 
+// The packed weight buffer of moe_prepack_weights (bf16): the routed and the
+// shared gate/up weights (w13), each 256-byte aligned and the size of its
+// canonical array. Only the gate/up GEMM reads packed weights: the down
+// GEMM on the packed layout measured slower than on the LDS-staged
+// canonical one (prefill layer, routed down 4.45 against 4.22 ms).
+struct PackedLayout {
+    size_t w13, sw13, total;
+};
+
+PackedLayout packed_layout(const moe_config* c) {
+    const size_t El = static_cast<size_t>(c->expert_end - c->expert_begin);
+    const size_t H = static_cast<size_t>(c->hidden), I = static_cast<size_t>(c->inter);
+    const size_t Is = static_cast<size_t>(c->shared_inter);
+    PackedLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align_up(bytes);
+        return at;
+    };
+    L.w13 = take(2 * El * 2 * I * H);
+    L.sw13 = take(2 * 2 * Is * H);
+    L.total = off;
+    return L;
+}
+
+const unsigned char* packed_ptr(const moe_weights* w, size_t off) {
+    return w->packed ? static_cast<const unsigned char*>(w->packed) + off : nullptr;
+}
+
 template <typename P>
 P* at(void* ws, size_t off) {
     return reinterpret_cast<P*>(static_cast<unsigned char*>(ws) + off);
@@ -339,7 +369,13 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
         StageTimer tm(MOE_STAGE_DOWN, s);
         return launch_quantised(c, Epi::PLAIN, g2, p2, s);
     }
-    const GemmPlan p1 = plan_gemm(el, Epi::SWIGLU, P, El, per_expert, static_cast<int>(I));
+    GemmPlan p1 = plan_gemm(el, Epi::SWIGLU, P, El, per_expert, static_cast<int>(I));
+    // 256 x 256 tiles read prepacked weights when the caller has them
+    const bool pf = p1.big && wt->packed;
+    if (pf) {
+        p1.big = 2;
+        g1.B = g1.B_shared = packed_ptr(wt, packed_layout(c).w13);
+    }
     if ((e = launch_schedule(g1, p1.bm, sched, s)) != hipSuccess) return e;
     {
         StageTimer tm(MOE_STAGE_GATE_UP, s);
@@ -362,7 +398,7 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
     GemmPlan p2 = plan_gemm(el, Epi::PLAIN, P, El, per_expert, static_cast<int>(H));
     if (p2.bm != p1.bm || p2.big != p1.big) {    // the down GEMM reuses the gate/up schedule's m-tiles
         if (p1.big) {
-            p2 = plan_gemm_big(Epi::PLAIN, P, El, static_cast<int>(H));
+            p2 = plan_gemm_big(Epi::PLAIN, P, El, static_cast<int>(H));   // the same 256 x 256 m-tiles
         } else {
             p2.big = 0;
             p2.bm = p1.bm;
@@ -482,8 +518,12 @@ hipError_t do_shared_ffn(const moe_config* c, int64_t T, const void* x, const mo
         return launch_gemm_cores(Epi::PLAIN, s2, q2, s);
     }
     const bool big = shared_big_tiles(c, T);
-    const GemmPlan q1 = big ? plan_gemm_big(Epi::SWIGLU, T, 1, static_cast<int>(Is))
-                            : plan_gemm(el, Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
+    // 256 x 256 tiles read prepacked weights when the caller has them
+    const bool pf = big && c->dtype == MOE_DTYPE_BF16 && wt->packed;
+    if (pf) s1.B = s1.B_shared = packed_ptr(wt, packed_layout(c).sw13);
+    const GemmPlan q1 = pf    ? plan_gemm_pf(Epi::SWIGLU, T, 1, static_cast<int>(Is))
+                        : big ? plan_gemm_big(Epi::SWIGLU, T, 1, static_cast<int>(Is))
+                              : plan_gemm(el, Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
     if (gate_up) {
         StageTimer tm(MOE_STAGE_SHARED_GATE_UP, s);
         if ((e = launch_gemm(el, Epi::SWIGLU, s1, q1, s)) != hipSuccess) return e;
@@ -649,6 +689,7 @@ hipError_t do_combine(const moe_config* c, int64_t T, const void* rows, const in
 
 bool weights_ok(const moe_config* c, const moe_weights* w) {
     if (!w || !w->w13 || !w->w2) return false;
+    if (w->packed && (c->dtype != MOE_DTYPE_BF16 || !aligned16(w->packed))) return false;
     if (!aligned16(w->w13) || !aligned16(w->w2)) return false;
     if (c->shared_inter > 0 && (!w->shared_w13 || !w->shared_w2 || !aligned16(w->shared_w13) ||
                                 !aligned16(w->shared_w2)))
@@ -784,6 +825,35 @@ int moe_workspace_bytes(const moe_config* cfg, int64_t max_tokens, size_t* bytes
     if (max_tokens < 0 || !bytes) return MOE_ERR_INVALID_ARG;
     *bytes = layout(cfg, max_tokens).total;
     return MOE_OK;
+}
+
+int moe_packed_weights_bytes(const moe_config* cfg, size_t* bytes) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    if (cfg->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    *bytes = packed_layout(cfg).total;
+    return MOE_OK;
+}
+
+int moe_prepack_weights(const moe_config* cfg, const moe_weights* canonical, void* packed, size_t packed_bytes,
+                        hipStream_t stream) {
+    int st = validate(cfg);
+    if (st) return st;
+    if (cfg->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    const moe_weights* w = canonical;
+    if (!w || !w->w13 || !packed) return MOE_ERR_INVALID_ARG;
+    if (cfg->shared_inter > 0 && !w->shared_w13) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(w->w13) || (reinterpret_cast<uintptr_t>(packed) % kAlign) ||
+        (cfg->shared_inter > 0 && !aligned16(w->shared_w13)))
+        return MOE_ERR_MISALIGNED;
+    const PackedLayout L = packed_layout(cfg);
+    if (packed_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    unsigned char* d = static_cast<unsigned char*>(packed);
+    const int El = cfg->expert_end - cfg->expert_begin, H = cfg->hidden, I = cfg->inter, Is = cfg->shared_inter;
+    hipError_t e = launch_prepack(w->w13, d + L.w13, El, 2 * I, H, I, true, stream);
+    if (e == hipSuccess && Is > 0) e = launch_prepack(w->shared_w13, d + L.sw13, 1, 2 * Is, H, Is, true, stream);
+    return hip_status(e);
 }
 
 int moe_router_gemm(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* router_bias,

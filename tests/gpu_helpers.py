@@ -37,7 +37,7 @@ def host(t):
 class Run:
     """Inputs of workload `w` on the GPU and the outputs of each HIP stage."""
 
-    def __init__(self, w, out_dtype="f32", gen_device="cpu", seed=0):
+    def __init__(self, w, out_dtype="f32", gen_device="cpu", seed=0, packed=False):
         self.w = w
         self.cfg = moe.config_from_workload(w, out_dtype=out_dtype)
         self.ocfg = O.Config.from_workload(w)
@@ -49,6 +49,11 @@ class Run:
         self.W = moe.make_weights(self.cfg, i["w13"], i["w2"], i["shared_w13"], i["shared_w2"],
                                   i.get("w13_scale"), i.get("w2_scale"), i.get("shared_w13_scale"),
                                   i.get("shared_w2_scale"))
+        if packed:
+            # the 256 x 256 tiles then read the prepacked copy of the weights
+            self.packed = moe.moe_prepack_weights(self.cfg, self.W)
+            self.W = moe.make_weights(self.cfg, i["w13"], i["w2"], i["shared_w13"], i["shared_w2"],
+                                      packed=self.packed)
 
     def stages(self):
         c, i, T = self.cfg, self.inp, self.T

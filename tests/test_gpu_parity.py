@@ -251,12 +251,12 @@ def test_layer_stages_match_oracle(name):
     check_layer(LAYER_CASES[name](), name)
 
 
-def check_layer(w, name):
+def check_layer(w, name, packed=False):
     """Every stage of one layer on the GPU against the oracle (shared by the
-    fixed cases here and the random sweep)."""
+    fixed cases here, the random sweep and the packed-weight cases)."""
     say("layer case", name, {k: w[k] for k in ("T", "hidden", "n_experts", "expert_begin", "expert_end", "dtype")})
     big = w["hidden"] >= 4096
-    run = Run(w, gen_device="cuda" if big else "cpu")
+    run = Run(w, gen_device="cuda" if big else "cpu", packed=packed)
     r = run.stages()
     tol = TOL[w["dtype"]]
     ref = run.oracle_forward(r["logits"])
