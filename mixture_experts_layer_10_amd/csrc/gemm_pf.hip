@@ -1,6 +1,7 @@
-// K5 / K6 at compute-bound shapes (bf16) on prepacked weights: grouped GEMM
-// with 256 x 256 tiles, the activation tile staged through a four-slot LDS
-// ring and the weights streamed from HBM straight into registers.
+// K5 at compute-bound shapes (bf16) on prepacked weights: the gate/up grouped
+// GEMM with its fused SwiGLU, 256 x 256 tiles, the activation tile staged
+// through a four-slot LDS ring and the weights streamed from HBM straight
+// into registers.
 //
 // What it computes is that of gemm.hip (Perplexity "Lower latency and higher
 // throughput with multi-node DeepSeek deployment", section "Roofline >
@@ -10,8 +11,8 @@
 // matrix cores, and what keeps them busy is hiding every load behind MFMAs:
 //
 //  * a workgroup of 4 wavefronts computes 256 rows x 4 weight panels of 64
-//    rows (SWIGLU: 32 gate rows + the 32 up rows of the same h columns;
-//    PLAIN: 64 consecutive rows); wavefront w owns panel w and all 256 rows,
+//    rows (32 gate rows + the 32 up rows of the same h columns: 128 h
+//    columns per tile); wavefront w owns panel w and all 256 rows,
 //    as 8 x 2 fragments of v_mfma_f32_32x32x16_bf16 (256 accumulators, held
 //    in the accumulation registers: one wavefront per SIMD);
 //  * the weights come from the prepacked layout (moe_prepack_weights), in
@@ -71,7 +72,6 @@ __device__ __forceinline__ float silu_mul_pf(float g, float u) { return g / (1.0
 // [6:4], lgkmcnt [11:8]).
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-template <Epi EPI>
 __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles) {
     // The LDS ring as four separate arrays, each indexed only by a constant
     // slot number: the compiler then knows that a fragment read of one slot
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
     // ---- weights: this wavefront's panel of the packed layout ----------------
     // A panel past the last one (N not a multiple of the tile) reads the last
     // panel; its results are dropped.
-    const int n_panels = EPI == Epi::SWIGLU ? a.inter / 32 : a.N / 64;
+    const int n_panels = a.inter / 32;
     int panel = nt * kNW + wave;
     panel = panel < n_panels ? panel : n_panels - 1;
     const unsigned char* Bw = static_cast<const unsigned char*>(shared ? a.B_shared : a.B) +
@@ -321,91 +321,55 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
     __syncthreads();
 
     // ---- epilogue: lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32)
-    // + e % 4 of each 32 x 32 fragment. Rows are staged 64 per LDS slot. ------
+    // + e % 4 of each 32 x 32 fragment: h = silu(gate) * up is formed in
+    // registers, rounded to bf16 and staged, 64 rows per LDS slot, as a
+    // row-major tile; the workgroup then writes whole 16-byte row pieces. ----
     const int64_t crow0 = shared ? m0 : static_cast<int64_t>(row0) + m0;
     unsigned char* Cb = static_cast<unsigned char*>(shared ? a.C_shared : a.C);
     const int lc = lane & 31, lh = lane >> 5;
-    constexpr int TC = EPI == Epi::SWIGLU ? 32 * kNW : 64 * kNW;     // output columns of the tile
-    auto epilogue = [&](auto f32_out) __attribute__((always_inline)) {
-        constexpr bool F32 = decltype(f32_out)::value;
-        constexpr int EB = F32 ? 4 : 2;
-        constexpr int PC = F32 ? TC / 2 : TC;                         // columns per pass (<= 512 B a row)
-        constexpr int PRB = PC * EB;
-        constexpr int GPR = PRB / 16;
-        static_assert(64 * PRB <= kSlotB, "64 staged rows per slot");
-        auto pass = [&](auto pass_c) __attribute__((always_inline)) {
-            constexpr int P = decltype(pass_c)::value;
-            if constexpr (P > 0) __syncthreads();                     // the previous pass's stores are done
-            auto put = [&](auto i_c) __attribute__((always_inline)) {
-                constexpr int I = decltype(i_c)::value;
-                if (I < nrb) {
-                    unsigned char* sl = slot(std::integral_constant<int, I / 2>{});
+    constexpr int TC = 32 * kNW;                                      // h columns of the tile
+    constexpr int PRB = TC * 2;                                       // staged bytes per row
+    constexpr int GPR = PRB / 16;
+    static_assert(64 * PRB <= kSlotB, "64 staged rows per slot");
+    auto put = [&](auto i_c) __attribute__((always_inline)) {
+        constexpr int I = decltype(i_c)::value;
+        if (I < nrb) {
+            unsigned char* sl = slot(std::integral_constant<int, I / 2>{});
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int r = (I % 2) * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);   // row within the slot
-                        unsigned char* row = sl + r * PRB;
-                        if constexpr (EPI == Epi::SWIGLU) {
-                            reinterpret_cast<uint16_t*>(row)[wave * 32 + lc] =
-                                f32_to_bf16_bits(silu_mul_pf(acc[I][0][e], acc[I][1][e]));
-                        } else {
-#pragma unroll
-                            for (int h = 0; h < 2; ++h) {
-                                const int col = wave * 64 + h * 32 - P * PC;   // the fragment's first column in the pass
-                                if (col >= 0 && col < PC) {                    // uniform
-                                    if constexpr (F32)
-                                        reinterpret_cast<float*>(row)[col + lc] = acc[I][h][e];
-                                    else
-                                        reinterpret_cast<uint16_t*>(row)[col + lc] = f32_to_bf16_bits(acc[I][h][e]);
-                                }
-                            }
-                        }
-                    }
-                }
-            };
-            put(std::integral_constant<int, 0>{});
-            put(std::integral_constant<int, 1>{});
-            put(std::integral_constant<int, 2>{});
-            put(std::integral_constant<int, 3>{});
-            put(std::integral_constant<int, 4>{});
-            put(std::integral_constant<int, 5>{});
-            put(std::integral_constant<int, 6>{});
-            put(std::integral_constant<int, 7>{});
-            __syncthreads();
-            // N and ldc are multiples of 8 (checked at launch), so a 16-byte
-            // piece lies wholly inside or wholly past the output's columns.
-            const int c0 = nt * TC + P * PC;
-            for (int q = tid; q < rows * GPR; q += kNT) {
-                const int r = q / GPR, gq = q % GPR;
-                const int col = c0 + gq * (16 / EB);
-                const unsigned char* sl = r < 64 ? s_a0 : r < 128 ? s_a1 : r < 192 ? s_a2 : s_a3;
-                if (col < a.N)
-                    st16(Cb + ((crow0 + r) * a.ldc + col) * EB, *reinterpret_cast<const vec16*>(sl + (r & 63) * PRB + gq * 16));
+            for (int e = 0; e < 16; ++e) {
+                const int r = (I % 2) * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);   // row within the slot
+                reinterpret_cast<uint16_t*>(sl + r * PRB)[wave * 32 + lc] =
+                    f32_to_bf16_bits(silu_mul_pf(acc[I][0][e], acc[I][1][e]));
             }
-        };
-        pass(std::integral_constant<int, 0>{});
-        if constexpr (F32) pass(std::integral_constant<int, 1>{});
-    };
-    if constexpr (EPI == Epi::PLAIN) {
-        if (a.out_f32) {
-            epilogue(std::true_type{});
-            return;
         }
+    };
+    put(std::integral_constant<int, 0>{});
+    put(std::integral_constant<int, 1>{});
+    put(std::integral_constant<int, 2>{});
+    put(std::integral_constant<int, 3>{});
+    put(std::integral_constant<int, 4>{});
+    put(std::integral_constant<int, 5>{});
+    put(std::integral_constant<int, 6>{});
+    put(std::integral_constant<int, 7>{});
+    __syncthreads();
+    // N and ldc are multiples of 8 (checked at launch), so a 16-byte piece
+    // lies wholly inside or wholly past the output's columns.
+    const int c0 = nt * TC;
+    for (int q = tid; q < rows * GPR; q += kNT) {
+        const int r = q / GPR, gq = q % GPR;
+        const int col = c0 + gq * 8;
+        const unsigned char* sl = r < 64 ? s_a0 : r < 128 ? s_a1 : r < 192 ? s_a2 : s_a3;
+        if (col < a.N)
+            st16(Cb + ((crow0 + r) * a.ldc + col) * 2, *reinterpret_cast<const vec16*>(sl + (r & 63) * PRB + gq * 16));
     }
-    epilogue(std::false_type{});
 }
 
-template <Epi EPI>
-hipError_t launch_pf_epi(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_pf_kernel<EPI>), dim3(static_cast<unsigned>(p.grid)), dim3(kNT), 0, s, a, p.n_tiles);
-    return hipGetLastError();
-}
-
-// Packed layout: element (row n, column k) of an [N_B, K] weight, for the
-// panel p, half h and lane l holding it (see moe_prepack_weights), sits at
-// byte ((p * K/16 + k/16) * 2 + h) * 1024 + l * 16 + (k % 8) * 2, with
-// l = n_in_half + 32 * ((k / 8) % 2).
+// Packed layout of a gate/up weight [2I, K] (moe_prepack_weights): element
+// (row n, column k) of panel p, half h (gate rows 32p.., up rows I + 32p..)
+// sits at byte ((p * K/16 + k/16) * 2 + h) * 1024 + l * 16 + (k % 8) * 2 with
+// lane l = (n - first row of the half) + 32 * ((k / 8) % 2).
 __global__ __launch_bounds__(256) void prepack_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                                                      int64_t n_chunks, int K, int inter, int swiglu) {
+                                                      int64_t n_chunks, int K, int inter) {
     // one thread per 16-byte packed chunk: (panel, k step, half, lane)
     for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < n_chunks;
          c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
@@ -415,7 +379,7 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint16_t* __restrict
         const int ksteps = K / 16;
         const int64_t p = ps / ksteps;
         const int s = static_cast<int>(ps - p * ksteps);
-        const int64_t n = swiglu ? (h ? inter : 0) + p * 32 + (l & 31) : p * 64 + h * 32 + (l & 31);
+        const int64_t n = (h ? inter : 0) + p * 32 + (l & 31);
         const int k = s * 16 + (l >> 5) * 8;
         st16(dst + c * 8, ld16(src + n * K + k));
     }
@@ -423,8 +387,8 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint16_t* __restrict
 
 }  // namespace
 
-GemmPlan plan_gemm_pf(Epi epi, int64_t rows_upper, int n_groups, int N) {
-    GemmPlan p = plan_gemm_big(epi, rows_upper, n_groups, N);
+GemmPlan plan_gemm_pf(int64_t rows_upper, int n_groups, int inter) {
+    GemmPlan p = plan_gemm_big(Epi::SWIGLU, rows_upper, n_groups, inter);
     p.nw = kNW;
     p.big = 2;
     return p;
@@ -432,21 +396,21 @@ GemmPlan plan_gemm_pf(Epi epi, int64_t rows_upper, int n_groups, int N) {
 
 hipError_t launch_gemm_pf(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     if (p.grid == 0) return hipSuccess;
-    if (a.K % kKB != 0 || a.N % 8 != 0 || a.ldc % 8 != 0) return hipErrorInvalidValue;
-    if (epi == Epi::SWIGLU ? a.inter % 32 != 0 : a.N % 64 != 0) return hipErrorInvalidValue;
+    if (epi != Epi::SWIGLU) return hipErrorInvalidValue;
+    if (a.K % kKB != 0 || a.N % 8 != 0 || a.ldc % 8 != 0 || a.inter % 32 != 0) return hipErrorInvalidValue;
     GemmArgs b = a;
     b.ksplit = 1;
-    return epi == Epi::SWIGLU ? launch_pf_epi<Epi::SWIGLU>(b, p, s) : launch_pf_epi<Epi::PLAIN>(b, p, s);
+    hipLaunchKernelGGL(gemm_pf_kernel, dim3(static_cast<unsigned>(p.grid)), dim3(kNT), 0, s, b, p.n_tiles);
+    return hipGetLastError();
 }
 
-hipError_t launch_prepack(const void* src, void* dst, int64_t n_experts, int n_rows, int K, int inter, bool swiglu,
-                          hipStream_t s) {
-    const int64_t per = static_cast<int64_t>(n_rows) * K / 8;      // 16-byte chunks per expert
+hipError_t launch_prepack(const void* src, void* dst, int64_t n_experts, int inter, int K, hipStream_t s) {
+    const int64_t per = static_cast<int64_t>(2 * inter) * K / 8;      // 16-byte chunks per expert
     for (int64_t e = 0; e < n_experts; ++e) {
         const int64_t blocks = std::min<int64_t>((per + 255) / 256, 8192);
         hipLaunchKernelGGL(prepack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                           static_cast<const uint16_t*>(src) + e * n_rows * K,
-                           static_cast<uint16_t*>(dst) + e * n_rows * K, per, K, inter, swiglu ? 1 : 0);
+                           static_cast<const uint16_t*>(src) + e * 2 * inter * K,
+                           static_cast<uint16_t*>(dst) + e * 2 * inter * K, per, K, inter);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

@@ -521,7 +521,7 @@ hipError_t do_shared_ffn(const moe_config* c, int64_t T, const void* x, const mo
     // 256 x 256 tiles read prepacked weights when the caller has them
     const bool pf = big && c->dtype == MOE_DTYPE_BF16 && wt->packed;
     if (pf) s1.B = s1.B_shared = packed_ptr(wt, packed_layout(c).sw13);
-    const GemmPlan q1 = pf    ? plan_gemm_pf(Epi::SWIGLU, T, 1, static_cast<int>(Is))
+    const GemmPlan q1 = pf    ? plan_gemm_pf(T, 1, static_cast<int>(Is))
                         : big ? plan_gemm_big(Epi::SWIGLU, T, 1, static_cast<int>(Is))
                               : plan_gemm(el, Epi::SWIGLU, T, 1, T, static_cast<int>(Is));
     if (gate_up) {
@@ -851,8 +851,8 @@ int moe_prepack_weights(const moe_config* cfg, const moe_weights* canonical, voi
     if (packed_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
     unsigned char* d = static_cast<unsigned char*>(packed);
     const int El = cfg->expert_end - cfg->expert_begin, H = cfg->hidden, I = cfg->inter, Is = cfg->shared_inter;
-    hipError_t e = launch_prepack(w->w13, d + L.w13, El, 2 * I, H, I, true, stream);
-    if (e == hipSuccess && Is > 0) e = launch_prepack(w->shared_w13, d + L.sw13, 1, 2 * Is, H, Is, true, stream);
+    hipError_t e = launch_prepack(w->w13, d + L.w13, El, I, H, stream);
+    if (e == hipSuccess && Is > 0) e = launch_prepack(w->shared_w13, d + L.sw13, 1, Is, H, stream);
     return hip_status(e);
 }
 

@@ -116,15 +116,14 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int ksplit, hipStream_t s);
 // Compute-bound shapes (bf16): 256 x 256 tiles through a 2-stage LDS ring.
 GemmPlan plan_gemm_big(Epi epi, int64_t rows_upper, int n_groups, int N);
 hipError_t launch_gemm_big(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
-// Compute-bound shapes (bf16) on prepacked weights (gemm_pf.hip): the same
-// 256 x 256 tiles and schedule as plan_gemm_big (big = 2), B read from the
-// packed layout of moe_prepack_weights.
-GemmPlan plan_gemm_pf(Epi epi, int64_t rows_upper, int n_groups, int N);
+// The gate/up GEMM at compute-bound shapes (bf16) on prepacked weights
+// (gemm_pf.hip): the same 256 x 256 tiles and schedule as plan_gemm_big
+// (big = 2), B read from the packed layout of moe_prepack_weights. SWIGLU only.
+GemmPlan plan_gemm_pf(int64_t rows_upper, int n_groups, int inter);
 hipError_t launch_gemm_pf(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
-// Packs n_experts consecutive [n_rows, K] bf16 weights (SWIGLU: gate rows
-// then up rows, inter each) into the packed layout.
-hipError_t launch_prepack(const void* src, void* dst, int64_t n_experts, int n_rows, int K, int inter, bool swiglu,
-                          hipStream_t s);
+// Packs n_experts consecutive gate/up weights [2 inter, K] (bf16) into the
+// packed layout.
+hipError_t launch_prepack(const void* src, void* dst, int64_t n_experts, int inter, int K, hipStream_t s);
 // The shared expert (one group of T rows, bf16) on 128 x 128 tiles that fit
 // beside the routed decode tiles on a CU (gemm_cores.hip); one persistent
 // workgroup per CU (`cus` = compute units of the device).

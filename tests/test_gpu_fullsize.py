@@ -1,6 +1,6 @@
 """Parity at the full workload sizes, in the launch configuration the
-benchmark times (moe_forward, bf16 output), and at 32 times the EP8 decode
-batch.
+benchmark times (moe_forward, bf16 output, prepacked gate/up weights for the
+bf16 layers), and at 32 times the EP8 decode batch.
 
 At these sizes the oracle cannot run the whole layer in seconds, so:
   * routing ids and gates of EVERY token are compared bit for bit with the
@@ -41,6 +41,10 @@ def test_full_size_forward(name):
     inp = make_inputs(w, device="cuda")
     Wt = moe.make_weights(cfg, inp["w13"], inp["w2"], inp["shared_w13"], inp["shared_w2"], inp.get("w13_scale"),
                           inp.get("w2_scale"), inp.get("shared_w13_scale"), inp.get("shared_w2_scale"))
+    if w["dtype"] == "bf16":
+        # as bench.py runs it: the gate/up GEMMs' 256 x 256 tiles read the prepacked copy
+        packed = moe.moe_prepack_weights(cfg, Wt)
+        Wt = moe.make_weights(cfg, inp["w13"], inp["w2"], inp["shared_w13"], inp["shared_w2"], packed=packed)
     ws = moe.workspace(cfg, T)
     y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
     logits = torch.empty(T, E, dtype=torch.float32, device="cuda")

@@ -20,19 +20,18 @@ from test_gpu_parity import _small, check_layer
 pytestmark = pytest.mark.gpu
 
 
-def _expected_packed(w, n_rows, K, inter, swiglu):
+def _expected_packed(w, n_rows, K, inter):
     """Documented layout: panel p, K step s, half h, lane l, element e holds
-    W[n][k] with n = (gate p*32 + l%32 | up inter + p*32 + l%32) for the
-    gate/up weight (or p*64 + 32 h + l%32 for a plain one), and
-    k = 16 s + 8 (l // 32) + e."""
+    W[n][k] with n = gate row p*32 + l%32 (h = 0) or up row inter + p*32 +
+    l%32 (h = 1), and k = 16 s + 8 (l // 32) + e."""
     W = w.reshape(n_rows, K)
-    n_panels = inter // 32 if swiglu else n_rows // 64
+    n_panels = inter // 32
     p = np.arange(n_panels)[:, None, None, None, None]
     s = np.arange(K // 16)[None, :, None, None, None]
     h = np.arange(2)[None, None, :, None, None]
     l = np.arange(64)[None, None, None, :, None]
     e = np.arange(8)[None, None, None, None, :]
-    n = np.where(h == 1, inter, 0) + p * 32 + l % 32 if swiglu else p * 64 + h * 32 + l % 32
+    n = np.where(h == 1, inter, 0) + p * 32 + l % 32
     k = s * 16 + (l // 32) * 8 + e
     return W[n, k].reshape(-1)
 
@@ -54,10 +53,10 @@ def test_prepack_layout_byte_exact(H, I, Is, El):
     al = lambda b: (b + 255) // 256 * 256
     off = 0
     for e in range(El):
-        want = _expected_packed(bits(w13[e]), 2 * I, H, I, True)
+        want = _expected_packed(bits(w13[e]), 2 * I, H, I)
         assert np.array_equal(got[off // 2 + e * 2 * I * H: off // 2 + (e + 1) * 2 * I * H], want), ("w13", e)
     off += al(2 * El * 2 * I * H)
-    assert np.array_equal(got[off // 2: off // 2 + 2 * Is * H], _expected_packed(bits(s13), 2 * Is, H, Is, True))
+    assert np.array_equal(got[off // 2: off // 2 + 2 * Is * H], _expected_packed(bits(s13), 2 * Is, H, Is))
     assert off + al(2 * 2 * Is * H) == nbytes
 
 
