@@ -225,7 +225,8 @@ int moe_route(const moe_config* cfg, int64_t T, const float* logits, const float
  *  offsets    [E_l + 1] out: exclusive prefix of counts; offsets[E_l] = R
  *  perm       [T*k] out: perm[row] = p for rows 0..R-1 (rest untouched)
  *  inv        [T*k] out: inv[p] = row, or -1 for non-local or dropped pairs
- * An expert id outside [0, E) is treated as non-local. */
+ * An expert id outside [0, E) is treated as non-local, and counted in the
+ * workspace's error word (see moe_dispatch_errors). */
 int moe_dispatch(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int32_t* raw_counts,
                  int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                  void* ws, size_t ws_bytes, hipStream_t stream);
@@ -312,6 +313,21 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
 int moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
                         const float* router_bias, const float* score_bias, const moe_weights* weights,
                         void* y, float* logits_out, int32_t* topk_ids_out, hipStream_t stream);
+
+/* moe_dispatch_errors: a diagnostic, never on the layer's path. Every
+ * dispatch (moe_dispatch, and the dispatch step of moe_forward and
+ * moe_forward_noalloc) counts the topk_ids entries outside [0, E) it meets
+ * and writes that count into an error word at the start of its workspace;
+ * such pairs are dropped (they reach no expert). This call waits for
+ * `stream` (hipStreamSynchronize), then copies the word of the last
+ * dispatch enqueued on that workspace before it into *bad_ids.
+ *  ws        the workspace the dispatch ran on (device), or NULL for the
+ *            array of moe_forward_noalloc on the current device
+ *  ws_bytes  its size (at least 256; ignored when ws is NULL)
+ * Before the first dispatch on a caller's workspace the word is undefined;
+ * a call with T == 0 launches nothing and leaves it unchanged. Errors:
+ * INVALID_ARG (bad_ids NULL), MISALIGNED, WORKSPACE_TOO_SMALL, HIP. */
+int moe_dispatch_errors(const void* ws, size_t ws_bytes, hipStream_t stream, int64_t* bad_ids);
 
 /* ---- Expert load statistics and placement ----------------------------------
  * Infra guide "Data parallelism and expert parallelism", section 5: under

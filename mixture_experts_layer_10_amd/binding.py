@@ -71,6 +71,7 @@ def lib():
             "moe_combine": (ctypes.c_int, [cfgp, i64, vp, i32p, fp, vp, vp, vp]),
             "moe_forward": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, wp, vp, fp, i32p, vp, ctypes.c_size_t, vp]),
             "moe_forward_noalloc": (ctypes.c_int, [cfgp, i64, vp, vp, fp, fp, wp, vp, fp, i32p, vp]),
+            "moe_dispatch_errors": (ctypes.c_int, [vp, ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_int64)]),
             "moe_packed_weights_bytes": (ctypes.c_int, [cfgp, ctypes.POINTER(ctypes.c_size_t)]),
             "moe_prepack_weights": (ctypes.c_int, [cfgp, wp, vp, ctypes.c_size_t, vp]),
             "moe_quantize_fp8": (ctypes.c_int, [cfgp, i64, vp, vp, fp, vp]),
@@ -360,6 +361,20 @@ def moe_forward_noalloc(cfg, x, w_router, router_bias, score_bias, weights, y, l
         _ptr(logits_out, torch.float32, (T, E), "logits_out", optional=True),
         _ptr(topk_ids_out, torch.int32, (T, cfg.top_k), "topk_ids_out", optional=True),
         _stream(stream)), "moe_forward_noalloc")
+
+
+def moe_dispatch_errors(ws=None, stream=None):
+    """Expert ids outside [0, E) met by the last dispatch on workspace `ws`
+    (a uint8 device tensor; None: the moe_forward_noalloc array of the current
+    device). Waits for the stream."""
+    n = ctypes.c_int64(-1)
+    if ws is None:
+        st = lib().moe_dispatch_errors(None, 0, _stream(stream), ctypes.byref(n))
+    else:
+        st = lib().moe_dispatch_errors(_ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream),
+                                       ctypes.byref(n))
+    _check(st, "moe_dispatch_errors")
+    return int(n.value)
 
 
 def moe_expert_load(cfg, topk_ids, load, stream=None):

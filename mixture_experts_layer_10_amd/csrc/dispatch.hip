@@ -12,9 +12,11 @@
 // taken in token order.
 //
 // Three launches, no atomics whose order reaches a result:
-//   1. per-chunk LDS histograms (a chunk is dispatch_chunk(P) consecutive pairs);
+//   1. per-chunk LDS histograms (a chunk is dispatch_chunk(P) consecutive pairs)
+//      and per-chunk counts of expert ids outside [0, E);
 //   2. one workgroup scans the histograms column-wise (per expert, over
-//      chunks) and across experts -> raw counts, counts, offsets;
+//      chunks) and across experts -> raw counts, counts, offsets, and sums
+//      the out-of-range counts into the workspace's error word;
 //   3. per chunk, stable in-chunk ranks from wavefront ballots, then
 //      row = offsets[e] + (earlier chunks' pairs of e) + in-chunk rank.
 #include "moe_device.h"
@@ -38,19 +40,26 @@ __device__ __forceinline__ int local_expert(int id, int E, int begin, int El) {
 
 __global__ __launch_bounds__(kThreads) void hist_kernel(DispatchArgs a) {
     extern __shared__ int s_hist[];
+    __shared__ int s_bad;
     const int El = a.El;
     for (int i = threadIdx.x; i < El; i += kThreads) s_hist[i] = 0;
+    if (threadIdx.x == 0) s_bad = 0;
     __syncthreads();
     const int64_t cl = dispatch_chunk(a.P);
     const int64_t p0 = static_cast<int64_t>(blockIdx.x) * cl;
     const int64_t p1 = min(p0 + cl, a.P);
+    int bad = 0;
     for (int64_t p = p0 + threadIdx.x; p < p1; p += kThreads) {
-        const int le = local_expert(a.ids[p], a.E, a.begin, El);
+        const int id = a.ids[p];
+        bad += (id < 0 || id >= a.E) ? 1 : 0;
+        const int le = local_expert(id, a.E, a.begin, El);
         if (le < El) atomicAdd(&s_hist[le], 1);
     }
+    if (bad) atomicAdd(&s_bad, bad);
     __syncthreads();
     int32_t* out = a.chunk_hist + static_cast<int64_t>(blockIdx.x) * El;
     for (int i = threadIdx.x; i < El; i += kThreads) out[i] = s_hist[i];
+    if (threadIdx.x == 0) a.chunk_bad[blockIdx.x] = s_bad;     // written every call: nothing to clear
 }
 
 // Per expert, the running sum of its chunk histograms down the chunks (->
@@ -62,9 +71,19 @@ template <bool STAGED>
 __global__ __launch_bounds__(kThreads) void scan_kernel(DispatchArgs a, int nchunk) {
     __shared__ int s_off[4 * kThreads];
     __shared__ int s_part[kThreads];
+    __shared__ int s_bad;
     extern __shared__ int s_hist[];                    // [nchunk * El] when STAGED
     const int El = a.El;
     const int64_t n = static_cast<int64_t>(nchunk) * El;
+    // the batch's out-of-range ids: the chunks' counts summed here, the total
+    // written after the barrier that follows the column walks
+    if (threadIdx.x == 0) s_bad = 0;
+    __syncthreads();
+    {
+        int bad = 0;
+        for (int c = threadIdx.x; c < nchunk; c += kThreads) bad += a.chunk_bad[c];
+        if (bad) atomicAdd(&s_bad, bad);
+    }
     if constexpr (STAGED) {
         // sixteen independent loads in flight per thread, then their stores
         constexpr int kBatch = 16;
@@ -108,7 +127,10 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(DispatchArgs a, int nchu
         s_off[e] = cnt;
     }
     __syncthreads();
-    if (threadIdx.x == 0) s_part[0] = s_off[El - 1];     // last count, kept for the total
+    if (threadIdx.x == 0) {
+        s_part[0] = s_off[El - 1];                       // last count, kept for the total
+        *a.bad_ids = s_bad;                              // written every call: nothing to clear
+    }
     __syncthreads();
     const int last = s_part[0];
     __syncthreads();

@@ -90,11 +90,16 @@ hipError_t launch_quantised(const moe_config* c, Epi epi, const GemmArgs& a, con
 
 // Workspace layout for up to T tokens; every region 256-byte aligned.
 struct Layout {
-    size_t logits, ids, w, raw, counts, offsets, perm, inv, chunk_hist, chunk_base, sched, partial;
+    size_t status;                      // the error word of moe_dispatch_errors (offset 0)
+    size_t logits, ids, w, raw, counts, offsets, perm, inv, chunk_hist, chunk_base, chunk_bad, sched, partial;
     size_t h, h_shared, rows, shared_out;
     size_t xq, xs, hs, hs_shared;       // FP8, MXFP4: quantised x and the scales of x and h
     size_t total;
 };
+
+// The workspace opens with a status region; its first int32 is the error
+// word: expert ids outside [0, E) met by the last dispatch on the workspace.
+constexpr size_t kStatusBytes = 256;
 
 int router_chunk(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 64 : 128; }
 
@@ -111,6 +116,7 @@ Layout layout(const moe_config* c, int64_t T) {
         off += align_up(bytes);
         return at;
     };
+    L.status = take(kStatusBytes);
     L.logits = take(sizeof(float) * T * E);
     L.ids = take(sizeof(int32_t) * P);
     L.w = take(sizeof(float) * P);
@@ -121,6 +127,7 @@ Layout layout(const moe_config* c, int64_t T) {
     L.inv = take(sizeof(int32_t) * P);
     L.chunk_hist = take(sizeof(int32_t) * nchunk * El);
     L.chunk_base = take(sizeof(int32_t) * nchunk * El);
+    L.chunk_bad = take(sizeof(int32_t) * nchunk);
     L.sched = take(sizeof(int32_t) * (El + 2));
     L.partial = take(sizeof(float) * splitk_partial_rows_upto(T, c->n_experts, c->hidden, router_chunk(c)) * E);
     L.h = take(static_cast<size_t>(act_bytes(c)) * P * c->inter);
@@ -275,6 +282,8 @@ hipError_t do_dispatch(const moe_config* c, int64_t T, const int32_t* ids, int32
     d.inv = inv;
     d.chunk_hist = at<int32_t>(ws, L.chunk_hist);
     d.chunk_base = at<int32_t>(ws, L.chunk_base);
+    d.chunk_bad = at<int32_t>(ws, L.chunk_bad);
+    d.bad_ids = at<int32_t>(ws, L.status);
     d.P = T * c->top_k;
     d.E = c->n_experts;
     d.El = c->expert_end - c->expert_begin;
@@ -946,6 +955,25 @@ int moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x, const v
     // created (the kernels are those moe_forward picks, so results are equal)
     return forward_body(cfg, T, x, w_router, router_bias, score_bias, weights, y, logits_out, topk_ids_out, ws,
                         stream, false);
+}
+
+int moe_dispatch_errors(const void* ws, size_t ws_bytes, hipStream_t stream, int64_t* bad_ids) {
+    if (!bad_ids) return MOE_ERR_INVALID_ARG;
+    const void* src = ws;
+    if (!ws) {
+        void* p = nullptr;                   // the moe_forward_noalloc array of the current device
+        if (scratch_address(&p) != hipSuccess) return MOE_ERR_HIP;
+        src = p;
+    } else {
+        if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+        if (ws_bytes < kStatusBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    }
+    int32_t word = 0;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipMemcpy(&word, src, sizeof(word), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    *bad_ids = word;
+    return MOE_OK;
 }
 
 int moe_quantize_fp8(const moe_config* cfg, int64_t rows, const void* x, uint8_t* q, float* scale,

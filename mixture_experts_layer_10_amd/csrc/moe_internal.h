@@ -34,6 +34,8 @@ struct DispatchArgs {
     int32_t* inv;             // [P]
     int32_t* chunk_hist;      // [nchunk, El] scratch
     int32_t* chunk_base;      // [nchunk, El] scratch
+    int32_t* chunk_bad;       // [nchunk] scratch: ids outside [0, E) per chunk
+    int32_t* bad_ids;         // [1]: their total over the batch (the error word)
     int64_t P;                // T * k
     int E, El, begin;
     int64_t cap;              // capacity, or INT64_MAX

@@ -169,6 +169,12 @@ static void rejections() {
           MOE_ERR_WORKSPACE_TOO_SMALL);
     CHECK(moe_forward_noalloc(&full, 340, FAKE, FAKE, nullptr, nullptr, &w, FAKE, nullptr, nullptr, nullptr) ==
           MOE_ERR_WORKSPACE_TOO_SMALL);
+    // the dispatch error word's diagnostic: argument checks before any HIP call
+    int64_t nbad = -1;
+    CHECK(moe_dispatch_errors(FAKE, 4096, nullptr, nullptr) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_dispatch_errors(static_cast<char*>(FAKE) + 4, 4096, nullptr, &nbad) == MOE_ERR_MISALIGNED);
+    CHECK(moe_dispatch_errors(FAKE, 255, nullptr, &nbad) == MOE_ERR_WORKSPACE_TOO_SMALL);
+    CHECK(nbad == -1);
     // an invalid config is reported by every entry point
     moe_config bad = dsv3(MOE_DTYPE_BF16);
     bad.n_group = 7;

@@ -163,6 +163,52 @@ def test_dispatch_bit_exact(T, E, k, b, e, cf, skew):
         assert np.all(o["perm"][R:] == -7)          # rows past R untouched
 
 
+@pytest.mark.parametrize("T,E,k,b,e", [(2048, 256, 8, 0, 32), (40000, 64, 6, 16, 48), (5, 16, 2, 0, 16)])
+def test_dispatch_error_word(T, E, k, b, e):
+    """Expert ids outside [0, E) are dropped like non-local pairs (the rest
+    of the dispatch bit-exact against the oracle) and counted in the
+    workspace's error word; a clean batch resets it, an empty one leaves it."""
+    rng = np.random.default_rng(T * 3 + E)
+    ids = _ids(T, E, k, rng, 0.0)
+    planted = rng.random(ids.shape) < 0.02
+    planted.flat[0] = True
+    bad_vals = np.array([-1, -E, E, E + 7, 2**31 - 1, -2**31], dtype=np.int64)
+    ids = ids.astype(np.int64)
+    ids[planted] = bad_vals[rng.integers(0, len(bad_vals), int(planted.sum()))]
+    ids = ids.astype(np.int32)
+    n_bad = int(planted.sum())
+    say("dispatch error-word case", T, E, k, b, e, "planted", n_bad)
+    cfg = moe.make_config(512, E, k, 128, expert_begin=b, expert_end=e, dtype="bf16")
+    ocfg = O.Config(hidden=512, n_experts=E, top_k=k, inter=128, expert_begin=b, expert_end=e)
+    ref = O.dispatch(ocfg, ids)
+    El = e - b
+    ws = moe.workspace(cfg, T)
+
+    def run(ids_np):
+        o = dict(raw_counts=torch.empty(El, dtype=torch.int32, device="cuda"),
+                 counts=torch.empty(El, dtype=torch.int32, device="cuda"),
+                 offsets=torch.empty(El + 1, dtype=torch.int32, device="cuda"),
+                 perm=torch.empty(max(1, ids_np.size), dtype=torch.int32, device="cuda"),
+                 inv=torch.empty(max(1, ids_np.size), dtype=torch.int32, device="cuda"))
+        moe.moe_dispatch(cfg, torch.from_numpy(ids_np).cuda(), o["raw_counts"], o["counts"], o["offsets"],
+                         o["perm"][:ids_np.size], o["inv"][:ids_np.size], ws)
+        return {k2: host(v) for k2, v in o.items()}
+
+    o = run(ids)
+    R = int(ref["offsets"][-1])
+    for key in ("raw_counts", "counts", "offsets"):
+        assert np.array_equal(o[key], ref[key]), key
+    assert np.array_equal(o["inv"][:ids.size], ref["inv"])
+    assert np.array_equal(o["perm"][:R], ref["perm"])
+    assert np.all(o["inv"][planted.reshape(-1)] == -1)
+    assert moe.moe_dispatch_errors(ws) == n_bad
+    run(np.zeros((0, k), dtype=np.int32))                  # T = 0: nothing launched, word unchanged
+    assert moe.moe_dispatch_errors(ws) == n_bad
+    clean = _ids(T, E, k, rng, 0.0)
+    run(clean)
+    assert moe.moe_dispatch_errors(ws) == 0
+
+
 # ---------------------------------------------------------------------------
 # Router GEMM, experts, combine, whole layer
 # ---------------------------------------------------------------------------

@@ -64,6 +64,7 @@ def test_noalloc_equals_forward_twice(name, out_dtype):
         ref, got = _run(w, T, out_dtype)
         for n in ("y", "l", "i"):
             assert torch.equal(got[n], ref[n]), (name, T, n)
+        assert moe.moe_dispatch_errors() == 0         # the static array's error word: routed ids are valid
 
 
 def test_noalloc_refuses_a_batch_past_its_scratch():
