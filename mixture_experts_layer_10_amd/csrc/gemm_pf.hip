@@ -31,8 +31,11 @@
 //    last two K steps run while the next stage's first fragments are read;
 //  * 16-byte granule q of LDS row r sits at q ^ ((r >> 1) & 7): the fragment
 //    reads (32 rows x one granule per lane half) are free of bank conflicts;
-//  * a group's rows are split evenly over its m-tiles; 32-row blocks past the
-//    tile's rows skip their MFMAs;
+//  * a group's rows are split evenly over its m-tiles; the K loop is
+//    instantiated for each count of 32-row blocks with data (1..8), so a
+//    tile reads and multiplies only its own blocks with no branch in the
+//    loop, and scheduling groups fix the order of each K step's MFMAs,
+//    fragment reads and loads;
 //  * the epilogue stages the tile in the idle LDS ring and writes whole
 //    16-byte pieces of rows.
 #include <utility>
@@ -189,40 +192,6 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = f32x16{};
 
-    // A fragments of K step t in buffer t % 2, all 8 blocks read whatever the
-    // tile's height (rows past its end hold copies of its last row), so
-    // that every path through the loop has the same LDS reads in flight and
-    // the compiler waits for exactly those each MFMA needs; only the MFMAs
-    // of blocks without rows are skipped (a branch on a uniform value).
-    bf16x8 af[2][8];
-    auto read = [&](auto u_c, auto t_c) __attribute__((always_inline)) {
-        constexpr int T = decltype(t_c)::value;
-        const unsigned char* st = slot(u_c) + f_off[T];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) af[T % 2][i] = frag(ld16(st + i * 32 * kRowB));
-    };
-    // MFMAs of K step t for row blocks [I0, I0 + 4); after each block's pair,
-    // ld(i) issues one load (unconditionally). With one wavefront per SIMD a
-    // load holds up the wavefront's issue while its addresses are taken in;
-    // behind an MFMA that time is hidden by the MFMA's own 32 cycles.
-    auto mfma = [&](auto u_c, auto t_c, auto i0_c, auto ld) __attribute__((always_inline)) {
-        constexpr int S = decltype(u_c)::value % 4;
-        constexpr int T = decltype(t_c)::value;
-        constexpr int I0 = decltype(i0_c)::value;
-        auto block = [&](auto i_c) __attribute__((always_inline)) {
-            constexpr int i = decltype(i_c)::value;
-            if (__builtin_expect(i < nrb, 1)) {          // full tiles: straight-line code
-                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[T % 2][i], frag(br[S][T][0]), acc[i][0], 0, 0, 0);
-                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[T % 2][i], frag(br[S][T][1]), acc[i][1], 0, 0, 0);
-            }
-            ld(i_c);
-        };
-        block(std::integral_constant<int, I0>{});
-        block(std::integral_constant<int, I0 + 1>{});
-        block(std::integral_constant<int, I0 + 2>{});
-        block(std::integral_constant<int, I0 + 3>{});
-    };
-    auto none = [](auto) {};
     // Wait until at most VM loads of this thread are outstanding (and, with
     // LGKM, its LDS reads are done), then, with BAR, a bare barrier (no
     // fence: the fills are waited for explicitly). The empty asm statements
@@ -252,15 +221,14 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
     // the prologue stands in for iterations -4..-1. Iteration j (stage j in
     // LDS slot j % 4 and ring slot j % 4; K step 0's fragments already read):
     //   wait for B(j)  [after it: A(j+1), B(j+1), A(j+2), B(j+2), A(j+3)]  vmcnt(40)
-    //   MFMAs of step 0 with the reads of step 1 between their halves, and
-    //   likewise steps 1 and 2;
-    //   (B(j+3), ring slot (j-1) % 4, last read by stage j-1, is issued
-    //   between the MFMAs of step 0)
+    //   K steps 0, 1 and 2, each with the fragment reads of the next step;
+    //   B(j+3) (ring slot (j-1) % 4, last read by stage j-1) is issued during
+    //   step 0;
     //   wait for A(j+1) [after it: B(j+1), A(j+2), B(j+2), A(j+3), B(j+3)] vmcnt(40)
     //   and this thread's LDS reads, then barrier: A(j+1) has landed for
     //   every wavefront and nobody reads slot j % 4 any more;
-    //   MFMAs of step 3 with A(j+4) (slot j % 4) issued between them, and
-    //   the reads of step 0 of stage j+1.
+    //   K step 3 with A(j+4) (into slot j % 4) issued during it, and the reads
+    //   of step 0 of stage j+1.
     // Loads past the last stage re-read it into free slots, so the wait
     // counts hold to the end.
     issue_a(C0{}, 0);
@@ -271,51 +239,119 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
     issue_b(C2{}, 2);
     issue_a(C3{}, 3);
     wait(std::integral_constant<int, 3 * kGroup>{}, Yes{});         // A(0) for every wavefront
-    read(C0{}, C0{});
 
-    // The fragment reads of the next K step sit between the two halves of a
-    // step's MFMAs, so that eight MFMAs cover their latency whatever wait the
-    // compiler puts before the next step's MFMAs (at a branch join it waits
-    // for every LDS read in flight). B(j + 3) is issued during K step 0 (its
-    // ring slot was last read by stage j - 1), A(j + 4) during K step 3,
-    // after the barrier that frees its LDS slot: one load per MFMA pair.
+    // The K loop for a tile of NRB 32-row blocks with data (1..8): only those
+    // blocks are read and multiplied, so the loop is branch-free, and
+    // scheduling groups lay out each K step explicitly. In a step the first
+    // NRB MFMAs alternate with the NRB fragment reads of the next step (so
+    // the reads have the step's second half to land: the compiler then waits
+    // for them only at the next step, when they are long done), and the
+    // second NRB MFMAs alternate with the stage's loads where the step issues
+    // any (with one wavefront per SIMD a load holds up the wavefront's issue
+    // while its addresses are taken in; behind an MFMA that time is hidden).
+    // Left to itself, the compiler bunched the loads and read each fragment
+    // just before its MFMA, waiting on every read.
     using L4 = std::integral_constant<int, 0>;
     using H4 = std::integral_constant<int, 4>;
-    auto iteration = [&](auto u_c, int kb) __attribute__((always_inline)) {
-        constexpr int U = decltype(u_c)::value;
-        using N = std::integral_constant<int, (U + 1) % 4>;
-        using P = std::integral_constant<int, (U + 3) % 4>;
-        auto ldb = [&](auto j_c) __attribute__((always_inline)) { issue_b_one(P{}, j_c, kb + 3); };
-        auto lda = [&](auto j_c) __attribute__((always_inline)) { issue_a_one(u_c, j_c, kb + 4); };
-        // B(j): after it A(j+1), B(j+1), A(j+2), B(j+2), A(j+3)
-        wait(std::integral_constant<int, 5 * kALoads>{}, No{});
-        mfma(u_c, C0{}, L4{}, ldb);
-        read(u_c, C1{});
-        mfma(u_c, C0{}, H4{}, ldb);
-        mfma(u_c, C1{}, L4{}, none);
-        read(u_c, C2{});
-        mfma(u_c, C1{}, H4{}, none);
-        mfma(u_c, C2{}, L4{}, none);
-        read(u_c, C3{});
-        mfma(u_c, C2{}, H4{}, none);
-        // A(j+1) for every wavefront: after it B(j+1), A(j+2), B(j+2), A(j+3), B(j+3)
-        wait(std::integral_constant<int, 5 * kALoads>{}, Yes{});
-        mfma(u_c, C3{}, L4{}, lda);
-        read(N{}, C0{});
-        mfma(u_c, C3{}, H4{}, lda);
+    auto kloop = [&](auto nrb_c) __attribute__((always_inline)) {
+        constexpr int NRB = decltype(nrb_c)::value;
+        bf16x8 af[2][NRB];
+        auto read = [&](auto u_c, auto t_c) __attribute__((always_inline)) {
+            constexpr int T = decltype(t_c)::value;
+            const unsigned char* st = slot(u_c) + f_off[T];
+#pragma unroll
+            for (int i = 0; i < NRB; ++i) af[T % 2][i] = frag(ld16(st + i * 32 * kRowB));
+        };
+        // the MFMAs of K step t for row blocks [I0, I0 + 4) (those below
+        // NRB); after each block, ld(i) issues load i of the stage
+        auto mfma = [&](auto u_c, auto t_c, auto i0_c, auto ld) __attribute__((always_inline)) {
+            constexpr int S = decltype(u_c)::value % 4;
+            constexpr int T = decltype(t_c)::value;
+            constexpr int I0 = decltype(i0_c)::value;
+            auto block = [&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                if constexpr (i < NRB) {
+                    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[T % 2][i], frag(br[S][T][0]), acc[i][0], 0, 0, 0);
+                    acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[T % 2][i], frag(br[S][T][1]), acc[i][1], 0, 0, 0);
+                }
+                ld(i_c);
+            };
+            block(std::integral_constant<int, I0>{});
+            block(std::integral_constant<int, I0 + 1>{});
+            block(std::integral_constant<int, I0 + 2>{});
+            block(std::integral_constant<int, I0 + 3>{});
+        };
+        auto none = [](auto) __attribute__((always_inline)) {};
+        // scheduling groups of one K step (mask 0x008 MFMA, 0x100 LDS read,
+        // 0x010 VMEM), with or without the stage's eight loads
+        auto groups = [&](auto loads_c) __attribute__((always_inline)) {
+#pragma unroll
+            for (int q = 0; q < NRB; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if constexpr (decltype(loads_c)::value) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if (q < NRB) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                }
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
+            }
+        };
+        auto iteration = [&](auto u_c, int kb) __attribute__((always_inline)) {
+            constexpr int U = decltype(u_c)::value;
+            using N = std::integral_constant<int, (U + 1) % 4>;
+            using P = std::integral_constant<int, (U + 3) % 4>;
+            auto ldb = [&](auto j_c) __attribute__((always_inline)) { issue_b_one(P{}, j_c, kb + 3); };
+            auto lda = [&](auto j_c) __attribute__((always_inline)) { issue_a_one(u_c, j_c, kb + 4); };
+            // B(j): after it A(j+1), B(j+1), A(j+2), B(j+2), A(j+3)
+            wait(std::integral_constant<int, 5 * kALoads>{}, No{});
+            mfma(u_c, C0{}, L4{}, ldb);
+            read(u_c, C1{});
+            mfma(u_c, C0{}, H4{}, ldb);
+            mfma(u_c, C1{}, L4{}, none);
+            read(u_c, C2{});
+            mfma(u_c, C1{}, H4{}, none);
+            mfma(u_c, C2{}, L4{}, none);
+            read(u_c, C3{});
+            mfma(u_c, C2{}, H4{}, none);
+            groups(Yes{});
+            groups(No{});
+            groups(No{});
+            // A(j+1) for every wavefront: after it B(j+1), A(j+2), B(j+2), A(j+3), B(j+3)
+            wait(std::integral_constant<int, 5 * kALoads>{}, Yes{});
+            mfma(u_c, C3{}, L4{}, lda);
+            read(N{}, C0{});
+            mfma(u_c, C3{}, H4{}, lda);
+            groups(Yes{});
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        read(C0{}, C0{});
+        // Whole groups of four stages with no conditional code; then the
+        // last zero to three stages.
+        int kb = 0;
+        for (; kb + 4 <= nkb; kb += 4) {
+            iteration(C0{}, kb);
+            iteration(C1{}, kb + 1);
+            iteration(C2{}, kb + 2);
+            iteration(C3{}, kb + 3);
+        }
+        if (kb < nkb) iteration(C0{}, kb);
+        if (kb + 1 < nkb) iteration(C1{}, kb + 1);
+        if (kb + 2 < nkb) iteration(C2{}, kb + 2);
     };
-    // Whole groups of four stages, no conditional code beyond the row-block
-    // checks; then the last zero to three stages.
-    int kb = 0;
-    for (; kb + 4 <= nkb; kb += 4) {
-        iteration(C0{}, kb);
-        iteration(C1{}, kb + 1);
-        iteration(C2{}, kb + 2);
-        iteration(C3{}, kb + 3);
+    switch (nrb) {
+        case 1: kloop(std::integral_constant<int, 1>{}); break;
+        case 2: kloop(std::integral_constant<int, 2>{}); break;
+        case 3: kloop(std::integral_constant<int, 3>{}); break;
+        case 4: kloop(std::integral_constant<int, 4>{}); break;
+        case 5: kloop(std::integral_constant<int, 5>{}); break;
+        case 6: kloop(std::integral_constant<int, 6>{}); break;
+        case 7: kloop(std::integral_constant<int, 7>{}); break;
+        default: kloop(std::integral_constant<int, 8>{}); break;
     }
-    if (kb < nkb) iteration(C0{}, kb);
-    if (kb + 1 < nkb) iteration(C1{}, kb + 1);
-    if (kb + 2 < nkb) iteration(C2{}, kb + 2);
     // no direct-load write may outlive the loop: the epilogue reuses the ring
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __syncthreads();
