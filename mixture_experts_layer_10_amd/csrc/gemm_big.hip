@@ -166,25 +166,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
     int a_off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a_off[i] = (b0 + i * bs) * 32 * kRowB;
-    // Fragments of k-steps 0..3 of a stage (4 x (4 A + NJ B) registers).
-    bf16x8 af[KSTEPS][4], bfr[KSTEPS][NJ];
-    auto read = [&](int slot, int t) __attribute__((always_inline)) {
-        const unsigned char* st = s_ring + slot * kStageB;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[t][i] = lds_frag(st + a_off[i] + f_off[t]);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) bfr[t][j] = lds_frag(st + b_base + j * 32 * kRowB + f_off[t]);
-    };
-    auto mfma = [&](int t) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i < nbw) {
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t][i], bfr[t][j], acc[i][j], 0, 0, 0);
-            }
-        }
-    };
     // Wait for this thread's LDS fills and LDS reads, then a bare barrier
     // (no fence: the fills are waited for explicitly). The empty asm
     // statements keep the compiler from moving memory accesses across it,
@@ -206,29 +187,83 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
     // of stage kb run. Every wait is for all of a thread's outstanding loads,
     // so the last two iterations simply issue none (measured: +0.4% on the
     // prefill layer against reloading the last stage).
-    issue(0, 0);
-    sync();
-    issue(min(1, last), 1);
-    read(0, 0);
-    read(0, 1);
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int s = kb & 1;
-        read(s, 2);
-        mfma(0);
-        read(s, 3);
-        mfma(1);
+    //
+    // The loop is instantiated for each count NBW of this wavefront's blocks
+    // with data (0..4; the two wavefront rows of a short tile can differ), so
+    // it holds no branch, reads only those blocks' fragments, and scheduling
+    // groups fix the order of each half: MFMAs alternate with the fragment
+    // reads (and after the barrier with the next stage's loads), which land
+    // while later MFMAs run. Every variant runs the same barriers.
+    auto kloop = [&](auto nbw_c) __attribute__((always_inline)) {
+        constexpr int NBW = decltype(nbw_c)::value;
+        // Fragments of k-steps 0..3 of a stage (4 x (NBW A + NJ B) registers).
+        bf16x8 af[KSTEPS][NBW > 0 ? NBW : 1], bfr[KSTEPS][NJ];
+        auto read = [&](int slot, int t) __attribute__((always_inline)) {
+            const unsigned char* st = s_ring + slot * kStageB;
+#pragma unroll
+            for (int i = 0; i < NBW; ++i) af[t][i] = lds_frag(st + a_off[i] + f_off[t]);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) bfr[t][j] = lds_frag(st + b_base + j * 32 * kRowB + f_off[t]);
+        };
+        auto mfma = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < NBW; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t][i], bfr[t][j], acc[i][j], 0, 0, 0);
+        };
+        // scheduling groups (mask 0x008 MFMA, 0x100 LDS read, 0x010 VMEM):
+        // M MFMAs, the first of them each followed by one of D reads, the
+        // rest by one of V loads; whatever is left over goes last
+        auto groups = [&](auto m_c, auto d_c, auto v_c) __attribute__((always_inline)) {
+            constexpr int M = decltype(m_c)::value, D = decltype(d_c)::value, V = decltype(v_c)::value;
+#pragma unroll
+            for (int q = 0; q < M; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (q < D) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                else if (q - D < V) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            }
+            if constexpr (D > M) __builtin_amdgcn_sched_group_barrier(0x100, D - M, 0);
+            if constexpr (V > 0 && D + V > M) __builtin_amdgcn_sched_group_barrier(0x010, D >= M ? V : D + V - M, 0);
+        };
+        constexpr int kRd = NBW + NJ;                          // fragment reads per k-step
+        constexpr int kMf = NBW * NJ;                          // MFMAs per k-step
+        issue(0, 0);
         sync();
-        if (kb + 2 <= last) issue(kb + 2, s);     // uniform
-        read(s ^ 1, 0);
-        read(s ^ 1, 1);
-        // raised issue priority for the MFMAs that overlap the next stage's
-        // loads and fragment reads: +0.8% at the prefill shape (raising it
-        // for every k-step's MFMAs, or for the loads instead, measured
-        // slower)
-        __builtin_amdgcn_s_setprio(1);
-        mfma(2);
-        mfma(3);
-        __builtin_amdgcn_s_setprio(0);
+        issue(min(1, last), 1);
+        read(0, 0);
+        read(0, 1);
+        for (int kb = 0; kb < nkb; ++kb) {
+            const int s = kb & 1;
+            read(s, 2);
+            mfma(0);
+            read(s, 3);
+            mfma(1);
+            groups(std::integral_constant<int, 2 * kMf>{}, std::integral_constant<int, 2 * kRd>{},
+                   std::integral_constant<int, 0>{});
+            sync();
+            if (kb + 2 <= last) issue(kb + 2, s);                // uniform
+            read(s ^ 1, 0);
+            read(s ^ 1, 1);
+            // raised issue priority for the MFMAs that overlap the next
+            // stage's loads and fragment reads: +0.8% at the prefill shape
+            // (raising it for every k-step's MFMAs, or for the loads
+            // instead, measured slower)
+            __builtin_amdgcn_s_setprio(1);
+            mfma(2);
+            mfma(3);
+            groups(std::integral_constant<int, 2 * kMf>{}, std::integral_constant<int, 2 * kRd>{},
+                   std::integral_constant<int, 0>{});
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
+        }
+    };
+    switch (nbw) {
+        case 0: kloop(std::integral_constant<int, 0>{}); break;
+        case 1: kloop(std::integral_constant<int, 1>{}); break;
+        case 2: kloop(std::integral_constant<int, 2>{}); break;
+        case 3: kloop(std::integral_constant<int, 3>{}); break;
+        default: kloop(std::integral_constant<int, 4>{}); break;
     }
     // With a single stage the prologue's second (clamped) load may still be
     // landing: no direct-load write may outlive the workgroup's LDS.
