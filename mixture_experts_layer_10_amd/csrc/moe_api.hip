@@ -620,22 +620,14 @@ hipError_t close_late_fork(const LateSharedDown& d) {
 
 hipError_t join_shared(SideStream* ss, hipStream_t s) { return hipStreamWaitEvent(s, ss->join, 0); }
 
-// The shared expert runs beside the routed experts unless both take the
-// 256 x 256 LDS-pipelined tiles: each of those holds a whole CU (128 KB of
-// LDS), so two such kernels only take turns on the CUs (measured: the bf16
-// prefill layer 1% slower overlapped). Every other pairing leaves the routed
-// GEMMs' matrix cores partly idle (bandwidth-bound tiles) for the shared
-// expert to fill: the EP8 decode layer and the capacity-limited fp8 layer run
-// faster overlapped (by about 20% and 4.5%).
-bool overlap_shared(const moe_config* c, int64_t T) {
-    if (c->shared_inter <= 0) return false;
-    const int64_t P = T * c->top_k;
-    const int El = c->expert_end - c->expert_begin;
-    const bool routed_big =
-        !quantised(c) &&
-        plan_gemm(gemm_elem(c), Epi::SWIGLU, P, El, (P + c->n_experts - 1) / c->n_experts, c->inter).big;
-    return !(routed_big && shared_big_tiles(c, T));
-}
+// The shared expert runs beside the routed experts whenever there is one.
+// With bandwidth-bound routed tiles it fills their idle matrix cores (the EP8
+// decode layer and the capacity-limited fp8 layer run about 20% and 4.5%
+// faster overlapped). At prefill both take the 256 x 256 tiles, which hold a
+// whole CU each, so the two only take turns on the CUs; what overlap still
+// gains there is the routed GEMMs' tails (the bf16 prefill layer 13.28 ->
+// 13.14 ms per step).
+bool overlap_shared(const moe_config* c, int64_t) { return c->shared_inter > 0; }
 
 // A shared expert that runs beside the routed experts launches its down GEMM
 // only once the routed gate/up GEMM has finished, so that it runs beside the
