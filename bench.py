@@ -66,11 +66,37 @@ KERNEL_SOURCES = {"bf16": ["gemm.hip", "gemm_big.hip", "gemm_pf.hip", "gemm_core
                   "mxfp4": ["gemm_mx.hip", "gemm_tile.h", "moe_internal.h", "moe_device.h"]}
 
 
+def _code_only(text):
+    """The source with its comments removed and blank runs collapsed, so that
+    the hash follows the code and not the comments (string and character
+    literals are kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            k = text.find("*/", i + 2)
+            i = n if k < 0 else k + 2
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def kernel_source_hash(dtype):
+    """Hash of the code (comments excluded) of the sources a kernel is built from."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[dtype]:
-        with open(os.path.join(ROOT, "mixture_experts_layer_10_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "mixture_experts_layer_10_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -27,9 +27,12 @@
 //  * SwiGLU tiles interleave gate and up rows so that each wavefront holds
 //    matching gate and up columns: h = silu(g) * u is formed in registers;
 //  * a group's rows are split evenly over its m-tiles, and 32-row blocks past
-//    a tile's real row count skip their MFMAs; in such a short tile the two
-//    wavefront rows take alternate blocks, so its busier row does
-//    ceil(blocks / 2) blocks of work rather than min(blocks, 4).
+//    a tile's real row count are neither read nor multiplied; in such a short
+//    tile the two wavefront rows take alternate blocks, so its busier row
+//    does ceil(blocks / 2) blocks of work rather than min(blocks, 4);
+//  * the K loop is instantiated for each count of a wavefront's blocks with
+//    data (0..4), so it holds no branch, and scheduling groups make its
+//    MFMAs alternate with the fragment reads.
 #include <utility>
 
 #include "gemm_tile.h"
