@@ -86,10 +86,6 @@ __device__ __forceinline__ void mfma_granule<Elem::F32>(const vec16& a, const ve
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w[c]), __uint_as_float(b.w[c]), acc, 0, 0, 0);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
-}
-
 // NW wavefronts per workgroup (4 or 8); with 8, two wavefronts share each
 // SIMD, so one can issue MFMAs while the other waits on memory.
 template <Elem EL, Epi EPI, int BM, int PD, int APD, bool SMAJOR, bool ASPLIT, int NW = 4>
@@ -430,15 +426,35 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(GemmArgs a) {
     }
 }
 
-// m-tile prefix over the groups: sched[g] = sum_{g' < g} ceil(rows_g' / bm).
-__global__ __launch_bounds__(kThreads) void schedule_kernel(GemmArgs a, int bm, int32_t* sched) {
-    __shared__ int s_v[4 * kThreads + 4];
+// m-tile prefix over the groups: sched[g] = sum_{g' < g} ceil(rows_g' / bm);
+// with splits, the XCD item ranges of each launch (XcdSplit). Items are
+// ordered group by group, and within a group column tile by column tile with
+// the m-tiles fastest (find_tile); an item of m-tile j costs the 32-row
+// blocks of that tile plus cost_q / 4 blocks.
+__global__ __launch_bounds__(kThreads) void schedule_kernel(GemmArgs a, int bm, int32_t* sched, XcdSplit sp0,
+                                                            XcdSplit sp1, int n_splits) {
+    constexpr int kMaxG = 4 * kThreads + 4;
+    __shared__ int s_v[kMaxG];
     __shared__ int s_part[kThreads];
+    __shared__ int s_blk[kMaxG];              // blocks with data over a group's m-tiles
+    __shared__ long long s_w[kMaxG + 1];      // work prefix over the groups
+    __shared__ long long s_wpart[kThreads];
+    __shared__ long long s_wlast;
+    __shared__ int s_b[8];
     const int n_groups = a.n_local + a.has_shared;
     for (int g = threadIdx.x; g < n_groups; g += kThreads) {
         int rows = a.T;
         if (!(a.has_shared && g == a.n_local) && a.offsets) rows = a.offsets[g + 1] - a.offsets[g];
-        s_v[g] = (rows + bm - 1) / bm;
+        const int mt = (rows + bm - 1) / bm;
+        s_v[g] = mt;
+        // balanced split (find_tile): m-tiles of tr rows, tr a multiple of
+        // 32, the last one the remainder (never empty, since tr <= bm)
+        int blk = 0;
+        if (mt > 0) {
+            const int tr = min(bm, ((rows + mt - 1) / mt + 31) & ~31);
+            blk = (mt - 1) * (tr / 32) + (rows - (mt - 1) * tr + 31) / 32;
+        }
+        s_blk[g] = blk;
     }
     __syncthreads();
     if (threadIdx.x == 0) s_part[0] = s_v[n_groups - 1];
@@ -447,7 +463,59 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(GemmArgs a, int bm, 
     __syncthreads();
     block_exclusive_scan<kThreads>(s_v, n_groups, s_part);
     for (int g = threadIdx.x; g < n_groups; g += kThreads) sched[g] = s_v[g];
-    if (threadIdx.x == 0) sched[n_groups] = s_v[n_groups - 1] + last;
+    const int total_mt = s_v[n_groups - 1] + last;
+    if (threadIdx.x == 0) sched[n_groups] = total_mt;
+    for (int i = 0; i < n_splits; ++i) {
+        const XcdSplit sp = i == 0 ? sp0 : sp1;
+        // work of group g: n_tiles columns of (4 x its blocks + cost_q x its m-tiles)
+        for (int g = threadIdx.x; g < n_groups; g += kThreads) {
+            const int mt = (g + 1 < n_groups ? s_v[g + 1] : total_mt) - s_v[g];
+            s_w[g] = static_cast<long long>(sp.n_tiles) * (4LL * s_blk[g] + static_cast<long long>(sp.cost_q) * mt);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) s_wlast = s_w[n_groups - 1];
+        __syncthreads();
+        block_exclusive_scan<kThreads>(s_w, n_groups, s_wpart);
+        const long long W = s_w[n_groups - 1] + s_wlast;
+        // XCD x (1..7) starts at the item where x / 8 of the work is done
+        if (threadIdx.x >= 1 && threadIdx.x < 8) {
+            const long long t = W * threadIdx.x / 8;
+            long long item = 0;
+            if (t < W) {
+                int lo = 0, hi = n_groups;                 // s_w[lo] <= t < s_w[hi] (s_w[n_groups] = W)
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_w[mid] <= t) lo = mid; else hi = mid;
+                }
+                const int mt = (lo + 1 < n_groups ? s_v[lo + 1] : total_mt) - s_v[lo];
+                const long long colw = 4LL * s_blk[lo] + static_cast<long long>(sp.cost_q) * mt;   // > 0
+                const long long rem = t - s_w[lo];
+                const long long c = rem / colw;            // column tile
+                const long long j = (rem - c * colw) * mt / colw;   // m-tile within it (pro rata)
+                item = static_cast<long long>(s_v[lo]) * sp.n_tiles + c * mt + j;
+            } else {
+                item = static_cast<long long>(total_mt) * sp.n_tiles;
+            }
+            s_b[threadIdx.x] = static_cast<int>(item);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            // monotone, range x within x * cap, then every range at most cap
+            // items: with 8 cap >= the item count every item keeps a slot
+            const int total = total_mt * sp.n_tiles;
+            int b[9];
+            b[0] = 0;
+            b[8] = total;
+            for (int x = 1; x < 8; ++x) {
+                int v = min(max(s_b[x], 0), total);
+                v = static_cast<int>(min(static_cast<long long>(v), static_cast<long long>(x) * sp.cap));
+                b[x] = max(v, b[x - 1]);
+            }
+            for (int x = 7; x >= 1; --x) b[x] = max(b[x], b[x + 1] - sp.cap);
+            for (int x = 0; x < 9; ++x) sp.out[x] = b[x];
+        }
+        __syncthreads();
+    }
 }
 
 template <Elem EL, Epi EPI, int BM, int PD, int APD, bool SMAJOR = false, bool ASPLIT = false, int NW = 4>
@@ -593,8 +661,16 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int ksplit, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_t s) {
-    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, s, a, bm, sched);
+hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_t s, const XcdSplit* splits,
+                           int n_splits) {
+    if (n_splits < 0 || n_splits > 2 || (n_splits > 0 && !splits)) return hipErrorInvalidValue;
+    XcdSplit sp[2] = {};
+    for (int i = 0; i < n_splits; ++i) {
+        if (splits[i].n_tiles <= 0 || splits[i].cap <= 0 || splits[i].cost_q < 0 || !splits[i].out)
+            return hipErrorInvalidValue;
+        sp[i] = splits[i];
+    }
+    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, s, a, bm, sched, sp[0], sp[1], n_splits);
     return hipGetLastError();
 }
 

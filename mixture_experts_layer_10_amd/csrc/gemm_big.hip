@@ -61,10 +61,6 @@ __device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_wav
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
-__device__ __forceinline__ float silu_mul_big(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
-}
-
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]).
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
@@ -305,7 +301,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
 #pragma unroll
                             for (int j = 0; j < NJ / 2; ++j)
                                 reinterpret_cast<uint16_t*>(row)[wn * (WB / 2) + j * 32 + lc] =
-                                    f32_to_bf16_bits(silu_mul_big(acc[i][j][e], acc[i][j + NJ / 2][e]));
+                                    f32_to_bf16_bits(silu_mul(acc[i][j][e], acc[i][j + NJ / 2][e]));
                         } else {
 #pragma unroll
                             for (int j = 0; j < NJ; ++j) {

@@ -195,7 +195,7 @@ void gemm_cores_kernel(GemmArgs a, int n_tiles, int m_tiles) {
                             if (col < a.N) {
                                 const float g = acc[i][0][e], u = acc[i][1][e];
                                 reinterpret_cast<uint16_t*>(a.C_shared)[rb + col] =
-                                    f32_to_bf16_bits(g / (1.0f + __expf(-g)) * u);
+                                    f32_to_bf16_bits(silu_mul(g, u));
                             }
                         } else {
 #pragma unroll

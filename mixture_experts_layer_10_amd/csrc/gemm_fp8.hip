@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NW * 64, ((BM <= 32 || NW == 8) ? 2 : 1)) void gemm
 #pragma unroll
                 for (int f = 0; f < NF / 2; ++f) {
                     const float gv = acc[i][f][v], uv = acc[i][f + NF / 2][v];
-                    h[i][f][v] = gv / (1.0f + __expf(-gv)) * uv;
+                    h[i][f][v] = silu_mul(gv, uv);
                     m = fmaxf(m, fabsf(h[i][f][v]));
                 }
 #pragma unroll
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_fp8_kernel(GemmArgs a, int n_
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const float gv = acc[i][j][v], uv = acc[i][j + 2][v];
-                    h[i][j][v] = gv / (1.0f + __expf(-gv)) * uv;
+                    h[i][j][v] = silu_mul(gv, uv);
                     m = fmaxf(m, fabsf(h[i][j][v]));
                 }
 #pragma unroll

@@ -363,7 +363,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_mx_kernel(GemmArgs a, int n
 #pragma unroll
                 for (int f = 0; f < NF / 2; ++f) {
                     const float gv = acc[i][f][v], uv = acc[i][f + NF / 2][v];
-                    h[i][f][v] = gv / (1.0f + __expf(-gv)) * uv;
+                    h[i][f][v] = silu_mul(gv, uv);
                     m = fmaxf(m, fabsf(h[i][f][v]));
                 }
 #pragma unroll

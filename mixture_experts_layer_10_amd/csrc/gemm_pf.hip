@@ -69,8 +69,6 @@ __device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_wav
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
-__device__ __forceinline__ float silu_mul_pf(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
-
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]).
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
@@ -375,7 +373,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
             for (int e = 0; e < 16; ++e) {
                 const int r = (I % 2) * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);   // row within the slot
                 reinterpret_cast<uint16_t*>(sl + r * PRB)[wave * 32 + lc] =
-                    f32_to_bf16_bits(silu_mul_pf(acc[I][0][e], acc[I][1][e]));
+                    f32_to_bf16_bits(silu_mul(acc[I][0][e], acc[I][1][e]));
             }
         }
     };

@@ -20,9 +20,11 @@ struct Tile {
 // m-tile: the workgroups that stream the same weight panel run side by side.
 // Items are dealt to the 8 XCDs in contiguous ranges (the hardware deals
 // workgroups round-robin over the XCDs), so neighbouring items share an XCD's
-// L2. Group row counts come from device memory (dispatch offsets and the
-// m-tile schedule), never from the host. Returns false for workgroups past
-// the last item (the grid is an upper bound). Uniform across the workgroup.
+// L2: equal item counts, or the ranges of a.xcd_range (cut by estimated work,
+// so that XCDs whose items have fewer rows are not left idle at the end).
+// Group row counts come from device memory (dispatch offsets and the m-tile
+// schedule), never from the host. Returns false for workgroups past the last
+// item (the grid is an upper bound). Uniform across the workgroup.
 //
 // With `balanced`, a group's rows are split into its m-tiles evenly (each
 // tile a multiple of 32 rows, at most BM) instead of BM, BM, ..., remainder:
@@ -34,10 +36,17 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& a, int n_tiles, int BM
     const int per_item = n_tiles * KS;                 // items per m-tile
     // A null schedule means a single group of T rows.
     const int total = (a.sched ? a.sched[n_groups] : (a.T + BM - 1) / BM) * per_item;
-    const int per_xcd = (total + 7) >> 3;
     const int slot = static_cast<int>(blockIdx.x >> 3);
-    if (slot >= per_xcd) return false;
-    const int L = static_cast<int>(blockIdx.x & 7) * per_xcd + slot;
+    int L;
+    if (a.xcd_range) {
+        const int x = static_cast<int>(blockIdx.x & 7);
+        L = a.xcd_range[x] + slot;
+        if (L >= a.xcd_range[x + 1]) return false;
+    } else {
+        const int per_xcd = (total + 7) >> 3;
+        if (slot >= per_xcd) return false;
+        L = static_cast<int>(blockIdx.x & 7) * per_xcd + slot;
+    }
     if (L >= total) return false;
     int g = 0, mt_begin = 0, mt_count = (a.T + BM - 1) / BM;
     if (a.sched) {

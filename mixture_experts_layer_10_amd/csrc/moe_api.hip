@@ -128,7 +128,7 @@ Layout layout(const moe_config* c, int64_t T) {
     L.chunk_hist = take(sizeof(int32_t) * nchunk * El);
     L.chunk_base = take(sizeof(int32_t) * nchunk * El);
     L.chunk_bad = take(sizeof(int32_t) * nchunk);
-    L.sched = take(sizeof(int32_t) * (El + 2));
+    L.sched = take(sizeof(int32_t) * (El + 2 + 2 * 9));    // m-tile prefix, then two sets of XCD ranges
     L.partial = take(sizeof(float) * splitk_partial_rows_upto(T, c->n_experts, c->hidden, router_chunk(c)) * E);
     L.h = take(static_cast<size_t>(act_bytes(c)) * P * c->inter);
     L.h_shared = take(static_cast<size_t>(act_bytes(c)) * T * c->shared_inter);
@@ -311,6 +311,19 @@ struct LateSharedDown {
 };
 hipError_t launch_late_shared_down(LateSharedDown* d, hipStream_t s);
 
+// Fixed cost of one 256 x 256 item over K, in quarters of the cost of one of
+// its 32-row blocks, from per-workgroup timelines of the prefill layer: each
+// 64-deep stage of an item of n blocks took f + b n, and the item about o
+// outside its K loop, so the fixed part is f / b + o / (b K / 64) blocks.
+//   packed gate/up kernel: f 0.28 us, b 0.163 us, o 13 us (K = 7168: 2.4);
+//   LDS-staged kernel (both operands through LDS, the down GEMM): f 0.93 us,
+//   b 0.104 us, o 10 us (K = 2048: 12).
+int item_cost_q(bool packed, int K) {
+    const double stages = K / 64.0;
+    const double blocks = packed ? 0.28 / 0.163 + 13.0 / (0.163 * stages) : 0.93 / 0.104 + 10.0 / (0.104 * stages);
+    return static_cast<int>(4.0 * blocks + 0.5);
+}
+
 hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const int32_t* perm,
                          const int32_t* offsets, const moe_weights* wt, void* rows, void* ws, hipStream_t s,
                          LateSharedDown* late) {
@@ -385,25 +398,6 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
         p1.big = 2;
         g1.B = g1.B_shared = packed_ptr(wt, packed_layout(c).w13);
     }
-    if ((e = launch_schedule(g1, p1.bm, sched, s)) != hipSuccess) return e;
-    {
-        StageTimer tm(MOE_STAGE_GATE_UP, s);
-        if ((e = launch_gemm(el, Epi::SWIGLU, g1, p1, s)) != hipSuccess) return e;
-    }
-    if (late && (e = launch_late_shared_down(late, s)) != hipSuccess) return e;
-
-    GemmArgs g2 = g1;
-    g2.A = g2.A_shared = at<void>(ws, L.h);
-    g2.perm = nullptr;
-    g2.gather = 0;
-    g2.B = g2.B_shared = wt->w2;
-    g2.b_stride = H * I;
-    g2.K = static_cast<int>(I);
-    g2.N = static_cast<int>(H);
-    g2.inter = 0;
-    g2.C = g2.C_shared = rows;
-    g2.ldc = static_cast<int>(H);
-    g2.out_f32 = c->dtype == MOE_DTYPE_F32;
     GemmPlan p2 = plan_gemm(el, Epi::PLAIN, P, El, per_expert, static_cast<int>(H));
     if (p2.bm != p1.bm || p2.big != p1.big) {    // the down GEMM reuses the gate/up schedule's m-tiles
         if (p1.big) {
@@ -417,6 +411,38 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
             p2.grid = ((P / p2.bm + El) * p2.n_tiles + 7) / 8 * 8;
         }
     }
+    if (p1.big) {
+        // 256 x 256 tiles: a group's m-tiles have 1..8 blocks of rows, so
+        // equal item counts would leave unequal work on the XCDs; both GEMMs
+        // get ranges cut by estimated work
+        int32_t* ranges = sched + El + 2;
+        const XcdSplit sp[2] = {
+            {p1.n_tiles, static_cast<int>(p1.grid / 8), item_cost_q(pf, static_cast<int>(H)), ranges},
+            {p2.n_tiles, static_cast<int>(p2.grid / 8), item_cost_q(false, static_cast<int>(I)), ranges + 9}};
+        if ((e = launch_schedule(g1, p1.bm, sched, s, sp, 2)) != hipSuccess) return e;
+        g1.xcd_range = ranges;
+    } else if ((e = launch_schedule(g1, p1.bm, sched, s)) != hipSuccess) {
+        return e;
+    }
+    {
+        StageTimer tm(MOE_STAGE_GATE_UP, s);
+        if ((e = launch_gemm(el, Epi::SWIGLU, g1, p1, s)) != hipSuccess) return e;
+    }
+    if (late && (e = launch_late_shared_down(late, s)) != hipSuccess) return e;
+
+    GemmArgs g2 = g1;
+    g2.xcd_range = g1.xcd_range ? g1.xcd_range + 9 : nullptr;
+    g2.A = g2.A_shared = at<void>(ws, L.h);
+    g2.perm = nullptr;
+    g2.gather = 0;
+    g2.B = g2.B_shared = wt->w2;
+    g2.b_stride = H * I;
+    g2.K = static_cast<int>(I);
+    g2.N = static_cast<int>(H);
+    g2.inter = 0;
+    g2.C = g2.C_shared = rows;
+    g2.ldc = static_cast<int>(H);
+    g2.out_f32 = c->dtype == MOE_DTYPE_F32;
     StageTimer tm(MOE_STAGE_DOWN, s);
     return launch_gemm(el, Epi::PLAIN, g2, p2, s);
 }

@@ -37,15 +37,27 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round-to-nearest-even float -> bf16 bits (finite inputs).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// float -> bf16 bits, rounded to nearest even: one v_cvt_pk_bf16_f32 on
+// gfx950 (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two floats -> packed bf16 (lo in the low half), one conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+// SwiGLU's activation product silu(g) * u = g * u / (1 + e^-g), with the
+// hardware exponential and reciprocal (1 ulp each) instead of a correctly
+// rounded division: six instructions, two of them transcendental, where the
+// division alone took ten. Every SwiGLU epilogue uses this one definition.
+// For g -> -inf the reciprocal of +inf gives 0, so the product is +-0.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // The 16-byte unit every kernel moves: one global or LDS vector access.
@@ -62,26 +74,26 @@ __device__ __forceinline__ void st16(void* p, const vec16& v) {
 
 // Exclusive prefix sum of v[0..n) in LDS by one workgroup of NT threads
 // (each thread sums a contiguous run, Hillis-Steele over the run totals).
-// s_part: NT ints of LDS scratch. Ends with a barrier.
-template <int NT>
-__device__ void block_exclusive_scan(int* v, int n, int* s_part) {
+// s_part: NT values of LDS scratch. Ends with a barrier.
+template <int NT, typename V>
+__device__ void block_exclusive_scan(V* v, int n, V* s_part) {
     const int per = (n + NT - 1) / NT;
     const int b = threadIdx.x * per;
-    int sum = 0;
+    V sum = 0;
     for (int i = 0; i < per; ++i)
         if (b + i < n) sum += v[b + i];
     s_part[threadIdx.x] = sum;
     __syncthreads();
     for (int off = 1; off < NT; off <<= 1) {
-        const int add = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
+        const V add = threadIdx.x >= off ? s_part[threadIdx.x - off] : V{0};
         __syncthreads();
         s_part[threadIdx.x] += add;
         __syncthreads();
     }
-    int run = s_part[threadIdx.x] - sum;
+    V run = s_part[threadIdx.x] - sum;
     for (int i = 0; i < per; ++i) {
         if (b + i < n) {
-            const int c = v[b + i];
+            const V c = v[b + i];
             v[b + i] = run;
             run += c;
         }

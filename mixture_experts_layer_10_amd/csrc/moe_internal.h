@@ -77,6 +77,10 @@ struct GemmArgs {
     // group n_local (if has_shared) has T rows.
     const int32_t* offsets;   // [n_local + 1], or null for a single dense group
     const int32_t* sched;     // [n_groups + 1] m-tile prefix
+    // Optional [9]: the launch's items dealt to the 8 XCDs by estimated work,
+    // XCD x taking items xcd_range[x] .. xcd_range[x+1]-1 (schedule_kernel);
+    // null: equal item counts per XCD.
+    const int32_t* xcd_range;
     int n_local, has_shared, T;
     int K;                    // reduction length
     int N;                    // output columns (I for SWIGLU, else N_B)
@@ -106,7 +110,21 @@ struct GemmPlan {
     int64_t grid;             // workgroups launched (upper bound on tiles * ksplit)
 };
 GemmPlan plan_gemm(Elem e, Epi epi, int64_t rows_upper, int n_groups, int64_t expected_rows_per_group, int N);
-hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_t s);
+// The m-tile schedule of a grouped GEMM: sched[g] = m-tiles of the groups
+// before g (row tiles of bm rows). Each XcdSplit also gets, for one launch of
+// 256 x 256 tiles on that schedule (balanced row split), the item ranges of
+// the 8 XCDs, cut where the estimated work (32-row blocks of an item plus
+// cost_q / 4 blocks of fixed cost per item) reaches x / 8 of the total, each
+// range at most `cap` items (the launch's workgroup slots per XCD, grid / 8,
+// so that every item has a workgroup).
+struct XcdSplit {
+    int n_tiles;              // column tiles per m-tile
+    int cap;                  // grid / 8
+    int cost_q;               // fixed cost per item, in quarter blocks
+    int32_t* out;             // [9] item boundaries
+};
+hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_t s, const XcdSplit* splits = nullptr,
+                           int n_splits = 0);
 hipError_t launch_gemm(Elem e, Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
 // Dense (single-group) PLAIN GEMM with fp32 output, split along K when the
 // tile grid alone would leave the GPU idle; `partial` must hold

@@ -96,3 +96,53 @@ def test_every_block_count_matches_oracle(shared_inter):
         err = O.rel_max_err(host(outs["packed"][1]), want)
         say("  shared expert: max|d|/rms", err)
         assert err < 2e-2
+
+
+@pytest.mark.parametrize("small_first", [True, False])
+def test_work_balanced_xcd_ranges_at_their_cap(small_first):
+    """The 256 x 256 launches deal their items to the 8 XCDs in ranges cut by
+    estimated work, each range capped at the launch's workgroup slots per XCD.
+    Half the experts with 20 rows (one-block items, cheap) and half with 1004
+    (four m-tiles of full blocks): cut by work alone, the ranges over the cheap
+    items would hold more items than an XCD has slots, so the cap decides
+    (at this shape the ranges over the cheap items reach it exactly in the
+    packed gate/up launch, 384 items, and in the down launch, 24). Every row
+    starts as NaN: a lost item leaves NaN rows, a wrong one differs from the
+    oracle."""
+    E, k, H, I, T = 64, 8, 256, 2048, 4096
+    sizes = [20] * 32 + [1004] * 32
+    if not small_first:
+        sizes = sizes[::-1]
+    say("xcd ranges: 32 experts x 20 rows, 32 x 1004, small first:", small_first)
+    cfg = moe.make_config(H, E, k, I, shared_inter=0, n_group=1, topk_group=1, dtype="bf16")
+    ocfg = O.Config(hidden=H, n_experts=E, top_k=k, inter=I, shared_inter=0, n_group=1, topk_group=1, act="bf16")
+    g = torch.Generator(device="cpu").manual_seed(99 + small_first)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    w13 = (torch.randn(E, 2 * I, H, generator=g) / H ** 0.5).to(torch.bfloat16)
+    w2 = (torch.randn(E, H, I, generator=g) / I ** 0.5).to(torch.bfloat16)
+    rng = np.random.default_rng(11)
+    R = sum(sizes)
+    assert R <= T * k
+    pairs = rng.permutation(T * k)[:R].astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    perm = np.full(T * k, -1, dtype=np.int32)
+    perm[:R] = pairs
+    dev = lambda a: torch.from_numpy(a).cuda()
+    Wc = moe.make_weights(cfg, w13.cuda(), w2.cuda())
+    packed = moe.moe_prepack_weights(cfg, Wc)
+    Wp = moe.make_weights(cfg, w13.cuda(), w2.cuda(), packed=packed)
+    ws = moe.workspace(cfg, T)
+    outs = {}
+    for name, W in (("canonical", Wc), ("packed", Wp)):
+        rows = torch.full((T * k, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+        moe.moe_expert_ffn(cfg, x.cuda(), dev(perm), dev(offsets), W, rows, None, ws)
+        torch.cuda.synchronize()
+        outs[name] = rows[:R].cpu()
+    assert torch.equal(outs["packed"].view(torch.int16), outs["canonical"].view(torch.int16))
+    got = host(outs["packed"]).astype(np.float64)
+    assert np.isfinite(got).all()                 # every row written
+    xh = host(x)
+    for e, n in enumerate(sizes):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        want = O.swiglu_expert(ocfg, xh[pairs[a:b] // k], host(w13[e]), host(w2[e]), I)
+        check_rows(got[a:b], want, "bf16")
