@@ -130,11 +130,12 @@ typedef struct moe_config {
  * MXFP4 weight rows are packed two E2M1 codes per byte, element 2i in the low
  * nibble: w13 [E_l, 2I, H/2] bytes, w2 [E_l, H, I/2] bytes.
  *  packed    BF16 only, optional (NULL: none): the buffer moe_prepack_weights
- *            filled from these same weights. With it, batches whose gate/up
+ *            filled from these same weights. With it, batches whose routed
  *            GEMMs take the 256 x 256 compute-bound tiles (hundreds of rows
- *            per expert: prefill shapes) stream the gate/up weights from it
- *            straight into registers; every other GEMM still reads the
- *            canonical arrays, which stay required. */
+ *            per expert: prefill shapes) stream the routed gate/up and down
+ *            weights and the shared gate/up weights from it straight into
+ *            registers; every other GEMM still reads the canonical arrays,
+ *            which stay required. */
 typedef struct moe_weights {
     const void* w13;
     const void* w2;
@@ -167,12 +168,15 @@ int moe_workspace_bytes(const moe_config* cfg, int64_t max_tokens, size_t* bytes
  * GroupGEMM"), and the 256 x 256 gate/up tiles then stream each weight panel
  * from HBM straight into registers, as MFMA operand fragments in the order
  * they are consumed. The packed buffer holds, 256-byte aligned and in this
- * order: the routed w13 [E_l] blocks and (when shared_inter > 0) the shared
- * w13 block, each the size of its canonical array. (The down projection is
- * read in canonical layout by every tile shape.)
- * A block of an [2I, K] gate/up weight is a sequence of 64-row panels, each
- * of K/16 steps of 2 KB: panel p holds gate rows 32p..32p+31 (half 0) and the
- * up rows I + 32p..I + 32p + 31 of the same h columns (half 1). Element
+ * order: the routed w13 [E_l] blocks, (when shared_inter > 0) the shared
+ * w13 block, and the routed w2 [E_l] blocks, each the size of its canonical
+ * array. (The shared expert's down projection, whose output is fp32, is read
+ * in canonical layout.)
+ * A block is a sequence of 64-row panels, each of K/16 steps of 2 KB, each
+ * panel's rows in two halves of 32: for a [2I, K] gate/up weight panel p
+ * holds gate rows 32p..32p+31 (half 0) and the up rows I + 32p..I + 32p + 31
+ * of the same h columns (half 1); for an [H, K] down weight (K = I) panel p
+ * holds rows 64p..64p+31 (half 0) and 64p+32..64p+63 (half 1). Element
  * (row n, column k) of half h, with n' its index within the half, sits at
  * byte ((p * K/16 + k/16) * 2 + h) * 1024 + (n' + 32 * ((k/8) % 2)) * 16
  * + (k % 8) * 2 of the block: one lane's 8 consecutive K values per 16 bytes,
@@ -183,7 +187,7 @@ int moe_workspace_bytes(const moe_config* cfg, int64_t max_tokens, size_t* bytes
  * other dtypes return MOE_ERR_UNSUPPORTED). Host only.
  * moe_prepack_weights: fills `packed` (device, 256-byte aligned, at least
  * packed_bytes = moe_packed_weights_bytes) from the canonical weights
- * (w13 and, with a shared expert, shared_w13; device). Asynchronous on
+ * (w13, w2 and, with a shared expert, shared_w13; device). Asynchronous on
  * `stream`; run once, before the weights are used. */
 int moe_packed_weights_bytes(const moe_config* cfg, size_t* bytes);
 int moe_prepack_weights(const moe_config* cfg, const moe_weights* canonical, void* packed, size_t packed_bytes,

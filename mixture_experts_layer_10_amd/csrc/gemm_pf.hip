@@ -1,7 +1,7 @@
-// K5 at compute-bound shapes (bf16) on prepacked weights: the gate/up grouped
-// GEMM with its fused SwiGLU, 256 x 256 tiles, the activation tile staged
-// through a four-slot LDS ring and the weights streamed from HBM straight
-// into registers.
+// K5 / K6 at compute-bound shapes (bf16) on prepacked weights: the gate/up
+// grouped GEMM with its fused SwiGLU and the routed down GEMM, 256 x 256
+// tiles, the activation tile staged through a four-slot LDS ring and the
+// weights streamed from HBM straight into registers.
 //
 // What it computes is that of gemm.hip (Perplexity "Lower latency and higher
 // throughput with multi-node DeepSeek deployment", section "Roofline >
@@ -11,8 +11,9 @@
 // matrix cores, and what keeps them busy is hiding every load behind MFMAs:
 //
 //  * a workgroup of 4 wavefronts computes 256 rows x 4 weight panels of 64
-//    rows (32 gate rows + the 32 up rows of the same h columns: 128 h
-//    columns per tile); wavefront w owns panel w and all 256 rows,
+//    rows (gate/up: 32 gate rows + the 32 up rows of the same h columns, 128
+//    h columns per tile; down: 64 consecutive output columns, 256 per tile);
+//    wavefront w owns panel w and all 256 rows,
 //    as 8 x 2 fragments of v_mfma_f32_32x32x16_bf16 (256 accumulators, held
 //    in the accumulation registers: one wavefront per SIMD);
 //  * the weights come from the prepacked layout (moe_prepack_weights), in
@@ -36,8 +37,9 @@
 //    tile reads and multiplies only its own blocks with no branch in the
 //    loop, and scheduling groups fix the order of each K step's MFMAs,
 //    fragment reads and loads;
-//  * the epilogue stages the tile in the idle LDS ring and writes whole
-//    16-byte pieces of rows.
+//  * the epilogue (h = silu(gate) * up, or the down GEMM's outputs as they
+//    are) stages the tile in the idle LDS ring and writes whole 16-byte
+//    pieces of rows.
 #include <utility>
 
 #include "gemm_tile.h"
@@ -73,6 +75,7 @@ __device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_wav
 // [6:4], lgkmcnt [11:8]).
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
+template <Epi EPI>
 __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles) {
     // The LDS ring as four separate arrays, each indexed only by a constant
     // slot number: the compiler then knows that a fragment read of one slot
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
     // ---- weights: this wavefront's panel of the packed layout ----------------
     // A panel past the last one (N not a multiple of the tile) reads the last
     // panel; its results are dropped.
-    const int n_panels = a.inter / 32;
+    const int n_panels = EPI == Epi::SWIGLU ? a.inter / 32 : a.N / 64;
     int panel = nt * kNW + wave;
     panel = panel < n_panels ? panel : n_panels - 1;
     const unsigned char* Bw = static_cast<const unsigned char*>(shared ? a.B_shared : a.B) +
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
     const int64_t crow0 = shared ? m0 : static_cast<int64_t>(row0) + m0;
     unsigned char* Cb = static_cast<unsigned char*>(shared ? a.C_shared : a.C);
     const int lc = lane & 31, lh = lane >> 5;
-    constexpr int TC = 32 * kNW;                                      // h columns of the tile
+    constexpr int TC = (EPI == Epi::SWIGLU ? 32 : 64) * kNW;          // output columns of the tile
     constexpr int PRB = TC * 2;                                       // staged bytes per row
     constexpr int GPR = PRB / 16;
     static_assert(64 * PRB <= kSlotB, "64 staged rows per slot");
@@ -372,8 +375,13 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int r = (I % 2) * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);   // row within the slot
-                reinterpret_cast<uint16_t*>(sl + r * PRB)[wave * 32 + lc] =
-                    f32_to_bf16_bits(silu_mul(acc[I][0][e], acc[I][1][e]));
+                if constexpr (EPI == Epi::SWIGLU) {
+                    reinterpret_cast<uint16_t*>(sl + r * PRB)[wave * 32 + lc] =
+                        f32_to_bf16_bits(silu_mul(acc[I][0][e], acc[I][1][e]));
+                } else {
+                    reinterpret_cast<uint16_t*>(sl + r * PRB)[wave * 64 + lc] = f32_to_bf16_bits(acc[I][0][e]);
+                    reinterpret_cast<uint16_t*>(sl + r * PRB)[wave * 64 + 32 + lc] = f32_to_bf16_bits(acc[I][1][e]);
+                }
             }
         }
     };
@@ -403,7 +411,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
 // sits at byte ((p * K/16 + k/16) * 2 + h) * 1024 + l * 16 + (k % 8) * 2 with
 // lane l = (n - first row of the half) + 32 * ((k / 8) % 2).
 __global__ __launch_bounds__(256) void prepack_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                                                      int64_t n_chunks, int K, int inter) {
+                                                      int64_t n_chunks, int K, int half_off, int pstride) {
     // one thread per 16-byte packed chunk: (panel, k step, half, lane)
     for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < n_chunks;
          c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
@@ -413,7 +421,7 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint16_t* __restrict
         const int ksteps = K / 16;
         const int64_t p = ps / ksteps;
         const int s = static_cast<int>(ps - p * ksteps);
-        const int64_t n = (h ? inter : 0) + p * 32 + (l & 31);
+        const int64_t n = h * half_off + p * pstride + (l & 31);
         const int k = s * 16 + (l >> 5) * 8;
         st16(dst + c * 8, ld16(src + n * K + k));
     }
@@ -430,11 +438,14 @@ GemmPlan plan_gemm_pf(int64_t rows_upper, int n_groups, int inter) {
 
 hipError_t launch_gemm_pf(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     if (p.grid == 0) return hipSuccess;
-    if (epi != Epi::SWIGLU) return hipErrorInvalidValue;
-    if (a.K % kKB != 0 || a.N % 8 != 0 || a.ldc % 8 != 0 || a.inter % 32 != 0) return hipErrorInvalidValue;
+    if (a.K % kKB != 0 || a.N % 8 != 0 || a.ldc % 8 != 0) return hipErrorInvalidValue;
+    if (epi == Epi::SWIGLU ? a.inter % 32 != 0 : (a.N % 64 != 0 || a.out_f32 || a.gather)) return hipErrorInvalidValue;
     GemmArgs b = a;
     b.ksplit = 1;
-    hipLaunchKernelGGL(gemm_pf_kernel, dim3(static_cast<unsigned>(p.grid)), dim3(kNT), 0, s, b, p.n_tiles);
+    if (epi == Epi::SWIGLU)
+        hipLaunchKernelGGL(gemm_pf_kernel<Epi::SWIGLU>, dim3(static_cast<unsigned>(p.grid)), dim3(kNT), 0, s, b, p.n_tiles);
+    else
+        hipLaunchKernelGGL(gemm_pf_kernel<Epi::PLAIN>, dim3(static_cast<unsigned>(p.grid)), dim3(kNT), 0, s, b, p.n_tiles);
     return hipGetLastError();
 }
 
@@ -444,7 +455,20 @@ hipError_t launch_prepack(const void* src, void* dst, int64_t n_experts, int int
         const int64_t blocks = std::min<int64_t>((per + 255) / 256, 8192);
         hipLaunchKernelGGL(prepack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                            static_cast<const uint16_t*>(src) + e * 2 * inter * K,
-                           static_cast<uint16_t*>(dst) + e * 2 * inter * K, per, K, inter);
+                           static_cast<uint16_t*>(dst) + e * 2 * inter * K, per, K, inter, 32);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_prepack_down(const void* src, void* dst, int64_t n_experts, int N, int K, hipStream_t s) {
+    const int64_t per = static_cast<int64_t>(N) * K / 8;              // 16-byte chunks per expert
+    for (int64_t e = 0; e < n_experts; ++e) {
+        const int64_t blocks = std::min<int64_t>((per + 255) / 256, 8192);
+        hipLaunchKernelGGL(prepack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(src) + e * static_cast<int64_t>(N) * K,
+                           static_cast<uint16_t*>(dst) + e * static_cast<int64_t>(N) * K, per, K, 32, 64);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

@@ -148,12 +148,14 @@ Layout layout(const moe_config* c, int64_t T) {
 }
 
 // The packed weight buffer of moe_prepack_weights (bf16): the routed and the
-// shared gate/up weights (w13), each 256-byte aligned and the size of its
-// canonical array. Only the gate/up GEMM reads packed weights: the down
-// GEMM on the packed layout measured slower than on the LDS-staged
-// canonical one (prefill layer, routed down 4.45 against 4.22 ms).
+// shared gate/up weights (w13), then the routed down weights (w2), each
+// 256-byte aligned and the size of its canonical array. The routed down GEMM
+// reads them on the packed tiles (gemm_pf.hip, plain epilogue): 4.00 against
+// 4.12-4.15 ms for the LDS-staged canonical tiles (prefill shape, no shared
+// expert beside it). The shared expert's down GEMM writes fp32 and keeps the
+// canonical tiles.
 struct PackedLayout {
-    size_t w13, sw13, total;
+    size_t w13, sw13, w2, total;
 };
 
 PackedLayout packed_layout(const moe_config* c) {
@@ -169,6 +171,7 @@ PackedLayout packed_layout(const moe_config* c) {
     };
     L.w13 = take(2 * El * 2 * I * H);
     L.sw13 = take(2 * 2 * Is * H);
+    L.w2 = take(2 * El * H * I);
     L.total = off;
     return L;
 }
@@ -418,7 +421,7 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
         int32_t* ranges = sched + El + 2;
         const XcdSplit sp[2] = {
             {p1.n_tiles, static_cast<int>(p1.grid / 8), item_cost_q(pf, static_cast<int>(H)), ranges},
-            {p2.n_tiles, static_cast<int>(p2.grid / 8), item_cost_q(false, static_cast<int>(I)), ranges + 9}};
+            {p2.n_tiles, static_cast<int>(p2.grid / 8), item_cost_q(pf, static_cast<int>(I)), ranges + 9}};
         if ((e = launch_schedule(g1, p1.bm, sched, s, sp, 2)) != hipSuccess) return e;
         g1.xcd_range = ranges;
     } else if ((e = launch_schedule(g1, p1.bm, sched, s)) != hipSuccess) {
@@ -443,6 +446,10 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
     g2.C = g2.C_shared = rows;
     g2.ldc = static_cast<int>(H);
     g2.out_f32 = c->dtype == MOE_DTYPE_F32;
+    if (pf && p2.big) {                           // the packed tiles, plain epilogue (bf16 rows)
+        g2.B = g2.B_shared = packed_ptr(wt, packed_layout(c).w2);
+        p2.big = 2;
+    }
     StageTimer tm(MOE_STAGE_DOWN, s);
     return launch_gemm(el, Epi::PLAIN, g2, p2, s);
 }
@@ -869,9 +876,9 @@ int moe_prepack_weights(const moe_config* cfg, const moe_weights* canonical, voi
     if (st) return st;
     if (cfg->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
     const moe_weights* w = canonical;
-    if (!w || !w->w13 || !packed) return MOE_ERR_INVALID_ARG;
+    if (!w || !w->w13 || !w->w2 || !packed) return MOE_ERR_INVALID_ARG;
     if (cfg->shared_inter > 0 && !w->shared_w13) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(w->w13) || (reinterpret_cast<uintptr_t>(packed) % kAlign) ||
+    if (!aligned16(w->w13) || !aligned16(w->w2) || (reinterpret_cast<uintptr_t>(packed) % kAlign) ||
         (cfg->shared_inter > 0 && !aligned16(w->shared_w13)))
         return MOE_ERR_MISALIGNED;
     const PackedLayout L = packed_layout(cfg);
@@ -880,6 +887,7 @@ int moe_prepack_weights(const moe_config* cfg, const moe_weights* canonical, voi
     const int El = cfg->expert_end - cfg->expert_begin, H = cfg->hidden, I = cfg->inter, Is = cfg->shared_inter;
     hipError_t e = launch_prepack(w->w13, d + L.w13, El, I, H, stream);
     if (e == hipSuccess && Is > 0) e = launch_prepack(w->shared_w13, d + L.sw13, 1, Is, H, stream);
+    if (e == hipSuccess) e = launch_prepack_down(w->w2, d + L.w2, El, H, I, stream);
     return hip_status(e);
 }
 

@@ -144,6 +144,9 @@ hipError_t launch_gemm_pf(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStre
 // Packs n_experts consecutive gate/up weights [2 inter, K] (bf16) into the
 // packed layout.
 hipError_t launch_prepack(const void* src, void* dst, int64_t n_experts, int inter, int K, hipStream_t s);
+// Packs n_experts consecutive down weights [N, K] (bf16): panels of 64 rows,
+// the two 32-row halves in place of the gate and up rows.
+hipError_t launch_prepack_down(const void* src, void* dst, int64_t n_experts, int N, int K, hipStream_t s);
 // The shared expert (one group of T rows, bf16) on 128 x 128 tiles that fit
 // beside the routed decode tiles on a CU (gemm_cores.hip); one persistent
 // workgroup per CU (`cus` = compute units of the device).

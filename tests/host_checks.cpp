@@ -105,8 +105,9 @@ static void sizing() {
         size_t pk = 0;
         const int st = moe_packed_weights_bytes(&c, &pk);
         if (dtype == MOE_DTYPE_BF16) {
-            // the routed and shared gate/up weights, 2 bytes each
-            CHECK(st == MOE_OK && pk == size_t{2} * (256 * size_t{2} * 2048 * 7168 + size_t{2} * 2048 * 7168));
+            // the routed and shared gate/up weights and the routed down weights, 2 bytes each
+            CHECK(st == MOE_OK && pk == size_t{2} * (256 * size_t{2} * 2048 * 7168 + size_t{2} * 2048 * 7168 +
+                                                     256 * size_t{7168} * 2048));
         } else {
             CHECK(st == MOE_ERR_UNSUPPORTED);
         }
@@ -159,6 +160,11 @@ static void rejections() {
     CHECK(moe_prepack_weights(&c, &w, FAKE, pk - 1, nullptr) == MOE_ERR_WORKSPACE_TOO_SMALL);
     CHECK(moe_prepack_weights(&c, &w, static_cast<char*>(FAKE) + 16, pk, nullptr) == MOE_ERR_MISALIGNED);
     CHECK(moe_prepack_weights(&c, nullptr, FAKE, pk, nullptr) == MOE_ERR_INVALID_ARG);
+    {
+        moe_weights no_down = w;               // the down weights are packed too: required
+        no_down.w2 = nullptr;
+        CHECK(moe_prepack_weights(&c, &no_down, FAKE, pk, nullptr) == MOE_ERR_INVALID_ARG);
+    }
     CHECK(moe_prepack_weights(&c8, &w, FAKE, pk, nullptr) == MOE_ERR_UNSUPPORTED);
     // operands past 4 GiB, and the allocation-free entry point's scratch limit
     moe_config full = dsv3(MOE_DTYPE_BF16);

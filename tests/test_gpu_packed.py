@@ -1,4 +1,5 @@
-"""The prepacked gate/up weight layout and the grouped GEMM that reads it.
+"""The prepacked gate/up and down weight layout and the grouped GEMMs that
+read it.
 
 moe_prepack_weights is pure data movement: its output is compared byte for
 byte with the layout the header documents, computed here with numpy indexing.
@@ -20,18 +21,19 @@ from test_gpu_parity import _small, check_layer
 pytestmark = pytest.mark.gpu
 
 
-def _expected_packed(w, n_rows, K, inter):
+def _expected_packed(w, n_rows, K, inter, down=False):
     """Documented layout: panel p, K step s, half h, lane l, element e holds
     W[n][k] with n = gate row p*32 + l%32 (h = 0) or up row inter + p*32 +
-    l%32 (h = 1), and k = 16 s + 8 (l // 32) + e."""
+    l%32 (h = 1) of a gate/up weight, row p*64 + 32 h + l%32 of a down
+    weight, and k = 16 s + 8 (l // 32) + e."""
     W = w.reshape(n_rows, K)
-    n_panels = inter // 32
+    n_panels = n_rows // 64 if down else inter // 32
     p = np.arange(n_panels)[:, None, None, None, None]
     s = np.arange(K // 16)[None, :, None, None, None]
     h = np.arange(2)[None, None, :, None, None]
     l = np.arange(64)[None, None, None, :, None]
     e = np.arange(8)[None, None, None, None, :]
-    n = np.where(h == 1, inter, 0) + p * 32 + l % 32
+    n = (p * 64 + h * 32 + l % 32) if down else (np.where(h == 1, inter, 0) + p * 32 + l % 32)
     k = s * 16 + (l // 32) * 8 + e
     return W[n, k].reshape(-1)
 
@@ -57,7 +59,11 @@ def test_prepack_layout_byte_exact(H, I, Is, El):
         assert np.array_equal(got[off // 2 + e * 2 * I * H: off // 2 + (e + 1) * 2 * I * H], want), ("w13", e)
     off += al(2 * El * 2 * I * H)
     assert np.array_equal(got[off // 2: off // 2 + 2 * Is * H], _expected_packed(bits(s13), 2 * Is, H, Is))
-    assert off + al(2 * 2 * Is * H) == nbytes
+    off += al(2 * 2 * Is * H)
+    for e in range(El):
+        want = _expected_packed(bits(w2[e]), H, I, None, down=True)
+        assert np.array_equal(got[off // 2 + e * H * I: off // 2 + (e + 1) * H * I], want), ("w2", e)
+    assert off + al(2 * El * H * I) == nbytes
 
 
 # layers whose expert GEMMs take the 256 x 256 tiles
