@@ -58,7 +58,9 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+/* 4: the packed weight buffer (moe_prepack_weights) also holds the routed
+ * down weights; a buffer packed by an earlier version is too short for it. */
+#define MOE_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 enum moe_status {

@@ -14,7 +14,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_MISALIGNED, ERR_HIP, ERR_ABI_MISMATCH = \
     0, -1, -2, -3, -4, -5, -6
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert moe.lib().moe_abi_version() == moe.ABI_VERSION == 3
+    assert moe.lib().moe_abi_version() == moe.ABI_VERSION == 4
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert moe.status_string(st) not in ("", "unknown status")
     assert moe.status_string(-99) == "unknown status"
