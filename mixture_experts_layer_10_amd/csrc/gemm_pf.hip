@@ -284,18 +284,19 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
         };
         auto none = [](auto) __attribute__((always_inline)) {};
         // scheduling groups of one K step (mask 0x008 MFMA, 0x100 LDS read,
-        // 0x010 VMEM), with or without the stage's eight loads
+        // 0x010 VMEM), with the step's LD loads (0: none)
         auto groups = [&](auto loads_c) __attribute__((always_inline)) {
+            constexpr int LD = decltype(loads_c)::value;
 #pragma unroll
             for (int q = 0; q < NRB; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            if constexpr (decltype(loads_c)::value) {
+            if constexpr (LD > 0) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
+                for (int q = 0; q < (LD > NRB ? LD : NRB); ++q) {
                     if (q < NRB) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                    if (q < LD) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
                 }
             } else {
                 __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
@@ -306,9 +307,15 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
             using N = std::integral_constant<int, (U + 1) % 4>;
             using P = std::integral_constant<int, (U + 3) % 4>;
             auto ldb = [&](auto j_c) __attribute__((always_inline)) { issue_b_one(P{}, j_c, kb + 3); };
-            auto lda = [&](auto j_c) __attribute__((always_inline)) { issue_a_one(u_c, j_c, kb + 4); };
-            // B(j): after it A(j+1), B(j+1), A(j+2), B(j+2), A(j+3)
-            wait(std::integral_constant<int, 5 * kALoads>{}, No{});
+            // only the loads of the tile's NRB blocks: load J of every
+            // wavefront fills rows 32 J .. 32 J + 31 of the slot
+            auto lda = [&](auto j_c) __attribute__((always_inline)) {
+                if constexpr (decltype(j_c)::value < NRB) issue_a_one(u_c, j_c, kb + 4);
+            };
+            // B(j): after it A(j+1), B(j+1), A(j+2), B(j+2), A(j+3). In the
+            // first iterations the prologue's A stages hold all eight loads,
+            // so these counts then wait for more than B(j): never less.
+            wait(std::integral_constant<int, 3 * NRB + 2 * kALoads>{}, No{});
             mfma(u_c, C0{}, L4{}, ldb);
             read(u_c, C1{});
             mfma(u_c, C0{}, H4{}, ldb);
@@ -318,15 +325,15 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
             mfma(u_c, C2{}, L4{}, none);
             read(u_c, C3{});
             mfma(u_c, C2{}, H4{}, none);
-            groups(Yes{});
-            groups(No{});
-            groups(No{});
+            groups(std::integral_constant<int, kALoads>{});
+            groups(std::integral_constant<int, 0>{});
+            groups(std::integral_constant<int, 0>{});
             // A(j+1) for every wavefront: after it B(j+1), A(j+2), B(j+2), A(j+3), B(j+3)
-            wait(std::integral_constant<int, 5 * kALoads>{}, Yes{});
+            wait(std::integral_constant<int, 3 * kALoads + 2 * NRB>{}, Yes{});
             mfma(u_c, C3{}, L4{}, lda);
             read(N{}, C0{});
             mfma(u_c, C3{}, H4{}, lda);
-            groups(Yes{});
+            groups(std::integral_constant<int, NRB>{});
             __builtin_amdgcn_sched_barrier(0);
         };
         read(C0{}, C0{});
