@@ -518,6 +518,37 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(GemmArgs a, int bm, 
     }
 }
 
+// The items of up to two launches on the schedule as tiles (find_tile's
+// arithmetic with the balanced row split, ksplit 1): table i gets entry L for
+// every item L below launch i's item count and cap i. One thread per item.
+__global__ __launch_bounds__(kThreads) void tile_table_kernel(GemmArgs a, int bm, int n0, int n1, int cap0, int cap1,
+                                                              int4* t0, int4* t1) {
+    const int n_groups = a.n_local + a.has_shared;
+    const int m_total = a.sched[n_groups];
+    const int L = static_cast<int>(blockIdx.x) * kThreads + static_cast<int>(threadIdx.x);
+    for (int i = 0; i < 2; ++i) {
+        const int n_tiles = i ? n1 : n0, cap = i ? cap1 : cap0;
+        int4* tab = i ? t1 : t0;
+        if (!tab || L >= m_total * n_tiles || L >= cap) continue;
+        int lo = 0, hi = n_groups;                     // sched[lo]*n_tiles <= L < sched[hi]*n_tiles
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.sched[mid] * n_tiles <= L) lo = mid; else hi = mid;
+        }
+        const int g = lo, mt_begin = a.sched[g], mt_count = a.sched[g + 1] - mt_begin;
+        const int local = L - mt_begin * n_tiles;
+        const int nt = local / mt_count, mt = local - nt * mt_count;
+        int rows_g = a.T, row0 = 0;
+        if (!(a.has_shared && g == a.n_local) && a.offsets) {
+            row0 = a.offsets[g];
+            rows_g = a.offsets[g + 1] - row0;
+        }
+        const int tr = min(bm, ((rows_g + mt_count - 1) / mt_count + 31) & ~31);
+        const int m0 = mt * tr;
+        tab[L] = int4{g | (nt << 16), row0, m0, min(tr, rows_g - m0)};
+    }
+}
+
 template <Elem EL, Epi EPI, int BM, int PD, int APD, bool SMAJOR = false, bool ASPLIT = false, int NW = 4>
 void launch_one(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     constexpr size_t lds = 2 * static_cast<size_t>(BM) * Tr<EL>::kRowG * 16;
@@ -671,6 +702,22 @@ hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_
         sp[i] = splits[i];
     }
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, s, a, bm, sched, sp[0], sp[1], n_splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_table(const GemmArgs& a, int bm, int n_launches, const int* n_tiles, const int* cap,
+                             int4* const* tables, hipStream_t s) {
+    if (n_launches < 1 || n_launches > 2 || !a.sched || bm <= 0) return hipErrorInvalidValue;
+    int mx = 0;
+    for (int i = 0; i < n_launches; ++i) {
+        if (n_tiles[i] <= 0 || n_tiles[i] >= (1 << 15) || cap[i] < 0 || !tables[i]) return hipErrorInvalidValue;
+        mx = std::max(mx, cap[i]);
+    }
+    if (mx == 0) return hipSuccess;
+    const bool two = n_launches > 1;
+    hipLaunchKernelGGL(tile_table_kernel, dim3(static_cast<unsigned>((mx + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       s, a, bm, n_tiles[0], two ? n_tiles[1] : 1, cap[0], two ? cap[1] : 0, tables[0],
+                       two ? tables[1] : nullptr);
     return hipGetLastError();
 }
 

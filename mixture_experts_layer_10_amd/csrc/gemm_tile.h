@@ -48,6 +48,18 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& a, int n_tiles, int BM
         L = static_cast<int>(blockIdx.x & 7) * per_xcd + slot;
     }
     if (L >= total) return false;
+    if (a.tiles) {
+        // one load (the search below takes a dependent load per step)
+        const int4 d = a.tiles[L];
+        t.g = d.x & 0xffff;
+        t.nt = d.x >> 16;
+        t.ks = 0;
+        t.shared = a.has_shared && t.g == a.n_local;
+        t.row0 = d.y;
+        t.m0 = d.z;
+        t.rows = d.w;
+        return true;
+    }
     int g = 0, mt_begin = 0, mt_count = (a.T + BM - 1) / BM;
     if (a.sched) {
         int lo = 0, hi = n_groups;                     // sched[lo]*per_item <= L < sched[hi]*per_item

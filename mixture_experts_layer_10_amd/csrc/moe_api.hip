@@ -91,7 +91,7 @@ hipError_t launch_quantised(const moe_config* c, Epi epi, const GemmArgs& a, con
 // Workspace layout for up to T tokens; every region 256-byte aligned.
 struct Layout {
     size_t status;                      // the error word of moe_dispatch_errors (offset 0)
-    size_t logits, ids, w, raw, counts, offsets, perm, inv, chunk_hist, chunk_base, chunk_bad, sched, partial;
+    size_t logits, ids, w, raw, counts, offsets, perm, inv, chunk_hist, chunk_base, chunk_bad, sched, tiles, partial;
     size_t h, h_shared, rows, shared_out;
     size_t xq, xs, hs, hs_shared;       // FP8, MXFP4: quantised x and the scales of x and h
     size_t total;
@@ -102,6 +102,19 @@ struct Layout {
 constexpr size_t kStatusBytes = 256;
 
 int router_chunk(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 64 : 128; }
+
+// Entries of the tile tables of the routed 256 x 256 launches for a batch of
+// T tokens: the gate/up launch's upper-bound grid, then the down launch's,
+// and 0 when the routed GEMMs do not take 256 x 256 tiles. Non-decreasing in
+// T (a workspace sized for T serves every smaller batch).
+int64_t big_tile_entries(const moe_config* c, int64_t T) {
+    if (c->dtype != MOE_DTYPE_BF16) return 0;
+    const int64_t El = c->expert_end - c->expert_begin, P = T * c->top_k;
+    const int64_t per_expert = (P + c->n_experts - 1) / c->n_experts;
+    const GemmPlan p1 = plan_gemm(Elem::BF16, Epi::SWIGLU, P, static_cast<int>(El), per_expert, static_cast<int>(c->inter));
+    if (!p1.big) return 0;
+    return p1.grid + plan_gemm_big(Epi::PLAIN, P, static_cast<int>(El), static_cast<int>(c->hidden)).grid;
+}
 
 Layout layout(const moe_config* c, int64_t T) {
     const int64_t E = c->n_experts, El = c->expert_end - c->expert_begin, k = c->top_k;
@@ -129,6 +142,7 @@ Layout layout(const moe_config* c, int64_t T) {
     L.chunk_base = take(sizeof(int32_t) * nchunk * El);
     L.chunk_bad = take(sizeof(int32_t) * nchunk);
     L.sched = take(sizeof(int32_t) * (El + 2 + 2 * 9));    // m-tile prefix, then two sets of XCD ranges
+    L.tiles = take(sizeof(int32_t) * 4 * big_tile_entries(c, T));
     L.partial = take(sizeof(float) * splitk_partial_rows_upto(T, c->n_experts, c->hidden, router_chunk(c)) * E);
     L.h = take(static_cast<size_t>(act_bytes(c)) * P * c->inter);
     L.h_shared = take(static_cast<size_t>(act_bytes(c)) * T * c->shared_inter);
@@ -414,6 +428,7 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
             p2.grid = ((P / p2.bm + El) * p2.n_tiles + 7) / 8 * 8;
         }
     }
+    const int4* down_tiles = nullptr;
     if (p1.big) {
         // 256 x 256 tiles: a group's m-tiles have 1..8 blocks of rows, so
         // equal item counts would leave unequal work on the XCDs; both GEMMs
@@ -424,6 +439,17 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
             {p2.n_tiles, static_cast<int>(p2.grid / 8), item_cost_q(pf, static_cast<int>(I)), ranges + 9}};
         if ((e = launch_schedule(g1, p1.bm, sched, s, sp, 2)) != hipSuccess) return e;
         g1.xcd_range = ranges;
+        // each item's tile in a table, so that a workgroup finds it with one
+        // load instead of a binary search of dependent loads over the schedule
+        // (2.2-2.7 us of every tile's start, measured)
+        if (p1.grid + p2.grid <= big_tile_entries(c, T)) {
+            int4* const tabs[2] = {at<int4>(ws, L.tiles), at<int4>(ws, L.tiles) + p1.grid};
+            const int nt[2] = {p1.n_tiles, p2.n_tiles};
+            const int cap[2] = {static_cast<int>(p1.grid), static_cast<int>(p2.grid)};
+            if ((e = launch_tile_table(g1, p1.bm, 2, nt, cap, tabs, s)) != hipSuccess) return e;
+            g1.tiles = tabs[0];
+            down_tiles = tabs[1];
+        }
     } else if ((e = launch_schedule(g1, p1.bm, sched, s)) != hipSuccess) {
         return e;
     }
@@ -435,6 +461,7 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
 
     GemmArgs g2 = g1;
     g2.xcd_range = g1.xcd_range ? g1.xcd_range + 9 : nullptr;
+    g2.tiles = down_tiles;
     g2.A = g2.A_shared = at<void>(ws, L.h);
     g2.perm = nullptr;
     g2.gather = 0;

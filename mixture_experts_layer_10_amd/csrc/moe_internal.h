@@ -81,6 +81,9 @@ struct GemmArgs {
     // XCD x taking items xcd_range[x] .. xcd_range[x+1]-1 (schedule_kernel);
     // null: equal item counts per XCD.
     const int32_t* xcd_range;
+    // Optional: the launch's items as tiles, tiles[L] = {g | nt << 16, row0,
+    // m0, rows} (launch_tile_table); null: found from the schedule.
+    const int4* tiles;
     int n_local, has_shared, T;
     int K;                    // reduction length
     int N;                    // output columns (I for SWIGLU, else N_B)
@@ -125,6 +128,11 @@ struct XcdSplit {
 };
 hipError_t launch_schedule(const GemmArgs& a, int bm, int32_t* sched, hipStream_t s, const XcdSplit* splits = nullptr,
                            int n_splits = 0);
+// Writes the items of up to two launches on a's schedule (row tiles of bm
+// rows, balanced split, n_tiles[i] column tiles, at most cap[i] items) as
+// tiles: tables[i][L] = {g | nt << 16, row0, m0, rows}.
+hipError_t launch_tile_table(const GemmArgs& a, int bm, int n_launches, const int* n_tiles, const int* cap,
+                             int4* const* tables, hipStream_t s);
 hipError_t launch_gemm(Elem e, Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
 // Dense (single-group) PLAIN GEMM with fp32 output, split along K when the
 // tile grid alone would leave the GPU idle; `partial` must hold
