@@ -86,8 +86,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
     const int g = tl.g, nt = tl.nt;
     const bool shared = tl.shared;
     const int row0 = tl.row0, m0 = tl.m0, rows = tl.rows;
-    const int K = a.K;
-    const int nkb = K / kKB;
+    const int K = a.K;                                             // row length of both operands
+    // With a K split (dense PLAIN fp32 only, checked at launch) the tile
+    // multiplies K slice tl.ks and writes its partial sums.
+    const int KS = a.ksplit;
+    const int k_len = K / KS;
+    const int64_t k_off = static_cast<int64_t>(tl.ks) * k_len * 2;  // bytes into each row
+    const int nkb = k_len / kKB;
     const int last = nkb - 1;
 
     // ---- direct-load sources: instruction j of wavefront w fills rows
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
     // loads the granule the swizzle places there --------------------------
     const int lrow = lane / kGran;                                 // row within the instruction's rows
     auto slot_granule = [&](int row) { return (lane % kGran) ^ swz(row); };
-    const unsigned char* Ag = static_cast<const unsigned char*>(shared ? a.A_shared : a.A);
+    const unsigned char* Ag = static_cast<const unsigned char*>(shared ? a.A_shared : a.A) + k_off;
     uint32_t aoff[kLoads];
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
@@ -107,8 +112,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
         else src = row0 + m0 + r;
         aoff[j] = src * static_cast<uint32_t>(K * 2) + slot_granule(rs) * 16;
     }
-    const unsigned char* Bg = shared ? static_cast<const unsigned char*>(a.B_shared)
-                                     : static_cast<const unsigned char*>(a.B) + static_cast<int64_t>(g) * a.b_stride * 2;
+    const unsigned char* Bg = (shared ? static_cast<const unsigned char*>(a.B_shared)
+                               : static_cast<const unsigned char*>(a.B) + static_cast<int64_t>(g) * a.b_stride * 2) +
+                              k_off;
     uint32_t boff[kLoads];
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
@@ -271,7 +277,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
     // ---- epilogue: lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32)
     // + e % 4 of each 32 x 32 fragment -----------------------------------------
     const int64_t crow0 = shared ? m0 : static_cast<int64_t>(row0) + m0;
-    unsigned char* Cb = static_cast<unsigned char*>(shared ? a.C_shared : a.C);
+    unsigned char* Cb = KS > 1 ? reinterpret_cast<unsigned char*>(a.partial + static_cast<int64_t>(tl.ks) * a.T * a.ldc)
+                               : static_cast<unsigned char*>(shared ? a.C_shared : a.C);
     const int lc = lane & 31, lh = lane >> 5;
     // Outputs are staged in the (now idle) LDS ring as a row-major tile, then
     // written as whole 16-byte pieces of rows: a lane's own fragment values
@@ -371,11 +378,42 @@ GemmPlan plan_gemm_big(Epi epi, int64_t rows_upper, int n_groups, int N) {
     return p;
 }
 
+// The router GEMM of a large batch (dense rows, fp32 out) on 256 x 256 tiles
+// split along K, so that its few m-tiles make about 256 workgroups: a split of
+// 2, 4 or 8 (at least 2, so that the partial-sum pass adds the bias), each
+// slice at least 8 stages long. ksplit 0: the batch has too few rows (fewer
+// than 32 tile rows of 256 rows) or K does not split; the caller takes
+// another plan. The partial sums take ksplit x T rows, at most
+// max(2 T, 131072) (with a split of 4 or 8, ksplit x m-tiles < 512).
+GemmPlan plan_router_big(int64_t T, int N, int K) {
+    GemmPlan p;
+    p.bm = kBM;
+    p.nw = 8;
+    p.smajor = 0;
+    p.big = 1;
+    p.ksplit = 0;
+    p.grid = 0;
+    p.n_tiles = (N + kBN - 1) / kBN;
+    const int64_t tiles = (T + kBM - 1) / kBM * p.n_tiles;
+    if (tiles < 32) return p;
+    int ks = 2;
+    while (ks < 8 && tiles * ks < 256) ks *= 2;
+    if (K % (ks * kKB) != 0 || K / ks < 8 * kKB) return p;
+    p.ksplit = ks;
+    p.grid = ((tiles * ks + 7) / 8) * 8;
+    return p;
+}
+
 hipError_t launch_gemm_big(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
     if (p.grid == 0) return hipSuccess;
     if (a.K % kKB != 0 || a.N % 8 != 0 || a.ldc % 8 != 0) return hipErrorInvalidValue;
     GemmArgs b = a;
-    b.ksplit = 1;
+    b.ksplit = p.ksplit < 1 ? 1 : p.ksplit;
+    // a K split: fp32 partial sums of dense rows (no groups, gather or shared
+    // expert), every slice whole stages
+    if (b.ksplit > 1 && (epi != Epi::PLAIN || !a.out_f32 || !a.partial || a.gather || a.sched || a.has_shared ||
+                         a.K % (b.ksplit * kKB) != 0))
+        return hipErrorInvalidValue;
     if (p.nw == 8)
         return epi == Epi::SWIGLU ? launch_big_epi<Epi::SWIGLU, 8>(b, p, s) : launch_big_epi<Epi::PLAIN, 8>(b, p, s);
     if (p.nw == 4)

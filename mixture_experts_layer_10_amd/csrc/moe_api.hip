@@ -116,6 +116,16 @@ int64_t big_tile_entries(const moe_config* c, int64_t T) {
     return p1.grid + plan_gemm_big(Epi::PLAIN, P, static_cast<int>(El), static_cast<int>(c->hidden)).grid;
 }
 
+// Rows of router partial sums for any batch up to T: the split-K plan of the
+// decode tiles, or, for a bf16 batch of 32 or more 256-row tiles, that of
+// the 256 x 256 tiles (at most max(2 T, 131072) rows).
+int64_t router_partial_rows_upto(const moe_config* c, int64_t T) {
+    int64_t rows = splitk_partial_rows_upto(T, c->n_experts, c->hidden, router_chunk(c));
+    if (gemm_elem(c) == Elem::BF16 && (T + 255) / 256 * ((c->n_experts + 255) / 256) >= 32)
+        rows = std::max(rows, std::max<int64_t>(2 * T, 131072));
+    return rows;
+}
+
 Layout layout(const moe_config* c, int64_t T) {
     const int64_t E = c->n_experts, El = c->expert_end - c->expert_begin, k = c->top_k;
     const int64_t P = T * k;
@@ -143,7 +153,7 @@ Layout layout(const moe_config* c, int64_t T) {
     L.chunk_bad = take(sizeof(int32_t) * nchunk);
     L.sched = take(sizeof(int32_t) * (El + 2 + 2 * 9));    // m-tile prefix, then two sets of XCD ranges
     L.tiles = take(sizeof(int32_t) * 4 * big_tile_entries(c, T));
-    L.partial = take(sizeof(float) * splitk_partial_rows_upto(T, c->n_experts, c->hidden, router_chunk(c)) * E);
+    L.partial = take(sizeof(float) * router_partial_rows_upto(c, T) * E);
     L.h = take(static_cast<size_t>(act_bytes(c)) * P * c->inter);
     L.h_shared = take(static_cast<size_t>(act_bytes(c)) * T * c->shared_inter);
     L.rows = take(static_cast<size_t>(row_bytes(c)) * P * c->hidden);
@@ -259,9 +269,20 @@ hipError_t do_router_gemm(const moe_config* c, int64_t T, const void* x, const v
     g.ldc = c->n_experts;
     g.bias = bias;
     g.out_f32 = 1;
+    g.partial = at<float>(ws, L.partial);
+    // A large bf16 batch: 256 x 256 tiles split along K (a few dozen m-tiles
+    // would leave most CUs idle); otherwise the decode tiles' split-K plan.
+    if (gemm_elem(c) == Elem::BF16) {
+        const GemmPlan pb = plan_router_big(T, c->n_experts, c->hidden);
+        if (pb.ksplit > 1) {
+            g.ksplit = pb.ksplit;
+            hipError_t e = launch_gemm_big(Epi::PLAIN, g, pb, s);
+            if (e == hipSuccess) e = launch_splitk_reduce(g, pb.ksplit, s);
+            return e;
+        }
+    }
     const GemmPlan p = plan_dense_splitk(T, c->n_experts, c->hidden, router_chunk(c));
     g.ksplit = p.ksplit;
-    g.partial = at<float>(ws, L.partial);
     hipError_t e = launch_gemm(gemm_elem(c), Epi::PLAIN, g, p, s);
     if (e == hipSuccess) e = launch_splitk_reduce(g, p.ksplit, s);
     return e;

@@ -144,6 +144,10 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int ksplit, hipStream_t s);
 // Compute-bound shapes (bf16): 256 x 256 tiles through a 2-stage LDS ring.
 GemmPlan plan_gemm_big(Epi epi, int64_t rows_upper, int n_groups, int N);
 hipError_t launch_gemm_big(Epi epi, const GemmArgs& a, const GemmPlan& p, hipStream_t s);
+// The router GEMM of a large bf16 batch on 256 x 256 tiles split along K
+// (gemm_big.hip; ksplit 0 when it does not apply; partial sums of ksplit x T
+// rows, at most max(2 T, 131072)), finished by launch_splitk_reduce.
+GemmPlan plan_router_big(int64_t T, int N, int K);
 // The gate/up GEMM at compute-bound shapes (bf16) on prepacked weights
 // (gemm_pf.hip): the same 256 x 256 tiles and schedule as plan_gemm_big
 // (big = 2), B read from the packed layout of moe_prepack_weights. SWIGLU only.

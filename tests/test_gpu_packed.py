@@ -75,6 +75,10 @@ PACKED_CASES = {
     # an output tile with two of its four panels past the last one, ragged tiles
     "ragged_k_and_panels": lambda: _small(T=11000, hidden=640, n_experts=16, expert_end=16, top_k=4, n_group=4,
                                           topk_group=2, inter=384, shared_inter=384, score_bias="zero"),
+    # two K stages in both GEMMs (hidden 128, inter 128): the shortest K loop
+    # (one column tile each, so 32768 tokens for enough 256-row tiles)
+    "two_k_stages": lambda: _small(T=32768, hidden=128, n_experts=16, expert_end=16, top_k=4, n_group=4,
+                                   topk_group=2, inter=128, shared_inter=128, score_bias="zero"),
     # capacity-capped groups of uneven size on the packed tiles, a local share
     "capacity_share": lambda: _small(T=4200, hidden=512, n_experts=16, expert_begin=2, expert_end=14, top_k=4,
                                      n_group=4, topk_group=2, inter=1024, shared_inter=512, capacity_factor=1.25,

@@ -213,6 +213,27 @@ def test_dispatch_error_word(T, E, k, b, e):
 # Router GEMM, experts, combine, whole layer
 # ---------------------------------------------------------------------------
 
+# Router GEMM of large bf16 batches: from 32 tiles of 256 rows on, 256 x 256
+# tiles split along K (8 slices at 32-63 tiles, 4 at 64-127); every logit
+# against the oracle's fp64 ones. 7900 tokens (31 tiles) stay on the decode
+# tiles; 16000 and 20000 end in a partial tile; 160 experts leave columns of
+# the one column tile past the last expert.
+@pytest.mark.parametrize("T,H,E,bias", [(7900, 4096, 256, True), (8000, 4096, 256, True),
+                                        (16000, 4096, 160, False), (20000, 4096, 256, True),
+                                        (16384, 7168, 256, True)])
+def test_router_gemm_large_batch_every_logit(T, H, E, bias):
+    say("router GEMM, large batch", dict(T=T, H=H, E=E, bias=bias))
+    cfg = moe.make_config(H, E, 8, 256, dtype="bf16")
+    g = torch.Generator(device="cuda").manual_seed(T + E)
+    x = torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
+    wr = (torch.randn(E, H, generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16)
+    b = torch.randn(E, generator=g, device="cuda") if bias else None
+    ws = moe.workspace(cfg, T)
+    logits = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_router_gemm(cfg, x, wr, b, logits, ws)
+    want = O.router_logits(host(x), host(wr), host(b))
+    assert O.rel_max_err(host(logits), want) < 1e-5
+
 LAYER_CASES = {
     "toy_fp32": lambda: workload("toy_fp32"),
     "toy_fp32_ragged": lambda: workload("toy_fp32", T=77),
