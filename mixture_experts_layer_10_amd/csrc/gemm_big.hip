@@ -12,8 +12,9 @@
 //    (8 by default, two per SIMD; 4 also built) form 2 x NW/2 and each
 //    computes four 32-row blocks x 512/NW weight rows as 32 x 32 fragments
 //    of v_mfma_f32_32x32x16_bf16;
-//  * both operands go HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR
-//    staging), K = 64 per stage: each row's 128 bytes are one whole cache
+//  * both operands go HBM/L2 -> LDS with buffer_load_dwordx4 ... lds (no
+//    VGPR staging; 32-bit row offsets against a buffer descriptor, the stage
+//    offset in a scalar), K = 64 per stage: each row's 128 bytes are one whole cache
 //    line, so a load instruction touches 8 lines (half-line loads, 16 rows of
 //    64 bytes, ran about a third slower); two stages (128 KB);
 //  * one barrier per stage, placed mid-stage: the MFMAs of a stage's last two
@@ -57,9 +58,6 @@ __device__ __forceinline__ bf16x8 lds_frag(const unsigned char* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const vec16*>(p));
 }
 
-__device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
 
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]).
@@ -132,14 +130,18 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_big_kernel(GemmArgs a, int n_
         }
         boff[j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + slot_granule(n) * 16;
     }
+    // Both operands through buffer descriptors (offsets below 4 GiB: the
+    // operand size limit): a load sends 32-bit row offsets, and the stage
+    // offset rides in a scalar.
+    const __amdgpu_buffer_rsrc_t ares = byte_buffer(Ag, 0xFFFFFFFFu), bres = byte_buffer(Bg, 0xFFFFFFFFu);
     auto issue = [&](int kb, int stage) __attribute__((always_inline)) {
         unsigned char* sa = s_ring + stage * kStageB;
         unsigned char* sb = sa + kBM * kRowB;
-        const uint32_t ko = static_cast<uint32_t>(kb) * kRowB;
+        const int ko = kb * kRowB;
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) load_lds16(Ag + aoff[j] + ko, sa + (NW * j + wave) * kRowsPerLoad * kRowB);
+        for (int j = 0; j < kLoads; ++j) buf_load_lds16(ares, aoff[j], ko, sa + (NW * j + wave) * kRowsPerLoad * kRowB);
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) load_lds16(Bg + boff[j] + ko, sb + (NW * j + wave) * kRowsPerLoad * kRowB);
+        for (int j = 0; j < kLoads; ++j) buf_load_lds16(bres, boff[j], ko, sb + (NW * j + wave) * kRowsPerLoad * kRowB);
     };
 
     // ---- fragment reads: lane l reads row (l % 32) of a 32-row block,

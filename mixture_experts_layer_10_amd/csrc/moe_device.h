@@ -72,6 +72,24 @@ __device__ __forceinline__ void st16(void* p, const vec16& v) {
     *reinterpret_cast<vec16*>(p) = v;
 }
 
+// Buffer descriptor of a raw byte range (word 3: data format 32, the one a
+// raw buffer access needs on this generation): loads through it take the
+// base from scalar registers and a 32-bit offset per lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_buffer(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                             0x00020000);
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ vec16 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    return __builtin_bit_cast(vec16, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+// 16 bytes per lane from a buffer straight into LDS (wave base lds_wave_base)
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff,
+                                               unsigned char* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff,
+                                             0, 0);
+}
+
 // Exclusive prefix sum of v[0..n) in LDS by one workgroup of NT threads
 // (each thread sums a contiguous run, Hillis-Steele over the run totals).
 // s_part: NT values of LDS scratch. Ends with a barrier.
