@@ -231,8 +231,11 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
     // LDS slot j % 4 and ring slot j % 4; K step 0's fragments already read):
     //   wait for B(j)  [after it: A(j+1), B(j+1), A(j+2), B(j+2), A(j+3)]  vmcnt(40)
     //   K steps 0, 1 and 2, each with the fragment reads of the next step;
-    //   B(j+3) (ring slot (j-1) % 4, last read by stage j-1) is issued during
-    //   step 0;
+    //   B(j+3) (ring slot (j-1) % 4, last read by stage j-1) is issued
+    //   three loads in step 0, three in step 1 and two in step 2 (all eight
+    //   in step 0: gate/up 6.3% slower; two per step with the last two after
+    //   the barrier, four per step with A(j+4) split over step 3 and the next
+    //   step 0, or 4-4-0 or 2-3-3 over steps 0-2: no better);
     //   wait for A(j+1) [after it: B(j+1), A(j+2), B(j+2), A(j+3), B(j+3)] vmcnt(40)
     //   and this thread's LDS reads, then barrier: A(j+1) has landed for
     //   every wavefront and nobody reads slot j % 4 any more;
@@ -257,7 +260,9 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
     // for them only at the next step, when they are long done), and the
     // second NRB MFMAs alternate with the stage's loads where the step issues
     // any (with one wavefront per SIMD a load holds up the wavefront's issue
-    // while its addresses are taken in; behind an MFMA that time is hidden).
+    // while its addresses are taken in; behind an MFMA that time is hidden;
+    // and the barrier keeps the four wavefronts in step, so a step's loads
+    // reach the CU's address unit together: few per step, spread over steps).
     // Left to itself, the compiler bunched the loads and read each fragment
     // just before its MFMA, waiting on every read.
     using L4 = std::integral_constant<int, 0>;
@@ -314,7 +319,16 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
             constexpr int U = decltype(u_c)::value;
             using N = std::integral_constant<int, (U + 1) % 4>;
             using P = std::integral_constant<int, (U + 3) % 4>;
-            auto ldb = [&](auto j_c) __attribute__((always_inline)) { issue_b_one(P{}, j_c, kb + 3); };
+            // B(j+3)'s eight loads spread over K steps 0, 1 and 2 (3, 3, 2),
+            // each after a block of the step's second half (all of them were
+            // issued by the wait for A(j+1), so its count holds)
+            auto ldb_at = [&](auto base_c, auto cnt_c) __attribute__((always_inline)) {
+                return [&, base_c, cnt_c](auto i_c) __attribute__((always_inline)) {
+                    constexpr int Q = decltype(i_c)::value - 4;
+                    if constexpr (Q >= 0 && Q < decltype(cnt_c)::value)
+                        issue_b_one(P{}, std::integral_constant<int, decltype(base_c)::value + Q>{}, kb + 3);
+                };
+            };
             // only the loads of the tile's NRB blocks: load J of every
             // wavefront fills rows 32 J .. 32 J + 31 of the slot
             auto lda = [&](auto j_c) __attribute__((always_inline)) {
@@ -324,18 +338,18 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
             // first iterations the prologue's A stages hold all eight loads,
             // so these counts then wait for more than B(j): never less.
             wait(std::integral_constant<int, 3 * NRB + 2 * kALoads>{}, No{});
-            mfma(u_c, C0{}, L4{}, ldb);
+            mfma(u_c, C0{}, L4{}, none);
             read(u_c, C1{});
-            mfma(u_c, C0{}, H4{}, ldb);
+            mfma(u_c, C0{}, H4{}, ldb_at(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{}));
             mfma(u_c, C1{}, L4{}, none);
             read(u_c, C2{});
-            mfma(u_c, C1{}, H4{}, none);
+            mfma(u_c, C1{}, H4{}, ldb_at(std::integral_constant<int, 3>{}, std::integral_constant<int, 3>{}));
             mfma(u_c, C2{}, L4{}, none);
             read(u_c, C3{});
-            mfma(u_c, C2{}, H4{}, none);
-            groups(std::integral_constant<int, kALoads>{});
-            groups(std::integral_constant<int, 0>{});
-            groups(std::integral_constant<int, 0>{});
+            mfma(u_c, C2{}, H4{}, ldb_at(std::integral_constant<int, 6>{}, std::integral_constant<int, 2>{}));
+            groups(std::integral_constant<int, 3>{});
+            groups(std::integral_constant<int, 3>{});
+            groups(std::integral_constant<int, 2>{});
             // A(j+1) for every wavefront: after it B(j+1), A(j+2), B(j+2), A(j+3), B(j+3)
             wait(std::integral_constant<int, 3 * kALoads + 2 * NRB>{}, Yes{});
             mfma(u_c, C3{}, L4{}, lda);
