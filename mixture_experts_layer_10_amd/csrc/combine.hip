@@ -20,6 +20,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 128;
+constexpr int kWideThreads = 448;      // rows of a multiple of 3584 columns
 constexpr int kBatch = 8;             // pairs whose rows are in flight together
 
 template <bool ROWS_F32>
@@ -60,8 +61,8 @@ __device__ __forceinline__ void unpack8(const vec16 (&raw)[ROWS_F32 ? 2 : 1], fl
     }
 }
 
-template <bool ROWS_F32, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+template <bool ROWS_F32, bool OUT_F32, int NT>
+__global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
     __shared__ int s_row[16];
     __shared__ float s_w[16];
     const int64_t t = blockIdx.x;
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     }
     __syncthreads();
     const int H = a.H;
-    for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
+    for (int c = threadIdx.x * 8; c < H; c += NT * 8) {
         float acc[8];
         if (a.shared) {
             load8<true>(a.shared, t * H + c, acc);
@@ -126,14 +127,23 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>(a.T)), block(kThreads);
-    if (a.rows_f32) {
-        if (a.out_f32) hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, a);
-    } else {
-        if (a.out_f32) hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, a);
-    }
+    const dim3 grid(static_cast<unsigned>(a.T));
+    // A row of a multiple of 3584 columns (DeepSeek-V3's 7168) in two passes
+    // of 448 threads: 0.510 against 0.527 ms for 128 threads (seven passes)
+    // at the bf16 prefill layer.
+    auto go = [&](auto nt_c) {
+        constexpr int NT = decltype(nt_c)::value;
+        const dim3 block(NT);
+        if (a.rows_f32) {
+            if (a.out_f32) hipLaunchKernelGGL((combine_kernel<true, true, NT>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((combine_kernel<true, false, NT>), grid, block, 0, s, a);
+        } else {
+            if (a.out_f32) hipLaunchKernelGGL((combine_kernel<false, true, NT>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((combine_kernel<false, false, NT>), grid, block, 0, s, a);
+        }
+    };
+    if (a.H % (kWideThreads * 8) == 0) go(std::integral_constant<int, kWideThreads>{});
+    else go(std::integral_constant<int, kThreads>{});
     return hipGetLastError();
 }
 
