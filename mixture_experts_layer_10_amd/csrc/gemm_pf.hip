@@ -312,11 +312,15 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             if constexpr (LD > 0) {
+                // a load after every second MFMA while both last, the rest after
+                constexpr int ST = (2 * LD <= NRB) ? 2 : 1;
 #pragma unroll
-                for (int q = 0; q < (LD > NRB ? LD : NRB); ++q) {
-                    if (q < NRB) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (q < LD) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                for (int q = 0; q < NRB; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if ((q + 1) % ST == 0 && (q + 1) / ST <= LD) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
                 }
+                constexpr int DONE = NRB / ST < LD ? NRB / ST : LD;
+                if constexpr (LD > DONE) __builtin_amdgcn_sched_group_barrier(0x010, LD - DONE, 0);
             } else {
                 __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
             }
