@@ -325,6 +325,19 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
                 __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
             }
         };
+        // a step's 2 NRB MFMAs, the first NRB each followed by a fragment
+        // read, and its LD loads spread evenly over all of them
+        auto groups_full = [&](auto loads_c) __attribute__((always_inline)) {
+            constexpr int LD = decltype(loads_c)::value;
+#pragma unroll
+            for (int q = 0; q < 2 * NRB; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (q < NRB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                // load k after MFMA (k + 1) * 2 NRB / LD - 1
+                if (LD > 0 && ((q + 1) * LD) / (2 * NRB) > (q * LD) / (2 * NRB))
+                    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            }
+        };
         auto iteration = [&](auto u_c, int kb) __attribute__((always_inline)) {
             constexpr int U = decltype(u_c)::value;
             using N = std::integral_constant<int, (U + 1) % 4>;
@@ -365,7 +378,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
             mfma(u_c, C3{}, L4{}, lda);
             read(N{}, C0{});
             mfma(u_c, C3{}, H4{}, lda);
-            groups(std::integral_constant<int, NRB>{});
+            groups_full(std::integral_constant<int, NRB>{});
             __builtin_amdgcn_sched_barrier(0);
         };
         read(C0{}, C0{});
