@@ -258,15 +258,19 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
 
     // The K loop for a tile of NRB 32-row blocks with data (1..8): only those
     // blocks are read and multiplied, so the loop is branch-free, and
-    // scheduling groups lay out each K step explicitly. In a step the first
-    // NRB MFMAs alternate with the NRB fragment reads of the next step (so
-    // the reads have the step's second half to land: the compiler then waits
-    // for them only at the next step, when they are long done), and the
-    // second NRB MFMAs alternate with the stage's loads where the step issues
-    // any (with one wavefront per SIMD a load holds up the wavefront's issue
-    // while its addresses are taken in; behind an MFMA that time is hidden;
-    // and the barrier keeps the four wavefronts in step, so a step's loads
-    // reach the CU's address unit together: few per step, spread over steps).
+    // scheduling groups lay out each K step explicitly. In a step the NRB
+    // fragment reads of the next step follow every second of the step's 2 NRB
+    // MFMAs (the compiler then waits for each only at the next step), and the
+    // stage's loads, where the step issues any, follow every second MFMA of
+    // the second half (step 3's over the whole step). With one wavefront per
+    // SIMD a load or read holds up the wavefront's issue while its addresses
+    // are taken in, which an MFMA in flight hides; and the barrier keeps the
+    // four wavefronts in step, so what a step issues reaches the CU's address
+    // unit and LDS together: few per step, spread out. (Measured, prefill
+    // layer: the weight loads all in step 0 against 3-3-2 over steps 0-2
+    // 4.3% slower; the reads one per MFMA in the first half against one per
+    // two MFMAs over the step about 1%; with the reads so spread the kernel
+    // spills 12 registers instead of 36.)
     // Left to itself, the compiler bunched the loads and read each fragment
     // just before its MFMA, waiting on every read.
     using L4 = std::integral_constant<int, 0>;
@@ -303,27 +307,22 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
         };
         auto none = [](auto) __attribute__((always_inline)) {};
         // scheduling groups of one K step (mask 0x008 MFMA, 0x100 LDS read,
-        // 0x010 VMEM), with the step's LD loads (0: none)
+        // 0x010 VMEM): the step's NRB fragment reads after every second of its
+        // 2 NRB MFMAs, and its LD loads (0: none) after every second MFMA of
+        // the second half
         auto groups = [&](auto loads_c) __attribute__((always_inline)) {
             constexpr int LD = decltype(loads_c)::value;
+            constexpr int ST = (2 * LD <= NRB) ? 2 : 1;
 #pragma unroll
-            for (int q = 0; q < NRB; ++q) {
+            for (int m = 0; m < 2 * NRB; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (m % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                const int q = m - NRB;
+                if (LD > 0 && q >= 0 && (q + 1) % ST == 0 && (q + 1) / ST <= LD)
+                    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
             }
-            if constexpr (LD > 0) {
-                // a load after every second MFMA while both last, the rest after
-                constexpr int ST = (2 * LD <= NRB) ? 2 : 1;
-#pragma unroll
-                for (int q = 0; q < NRB; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if ((q + 1) % ST == 0 && (q + 1) / ST <= LD) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-                }
-                constexpr int DONE = NRB / ST < LD ? NRB / ST : LD;
-                if constexpr (LD > DONE) __builtin_amdgcn_sched_group_barrier(0x010, LD - DONE, 0);
-            } else {
-                __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
-            }
+            constexpr int DONE = LD > 0 ? (NRB / ST < LD ? NRB / ST : LD) : 0;
+            if constexpr (LD > DONE) __builtin_amdgcn_sched_group_barrier(0x010, LD - DONE, 0);
         };
         // a step's 2 NRB MFMAs, the first NRB each followed by a fragment
         // read, and its LD loads spread evenly over all of them
@@ -332,7 +331,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_pf_kernel(GemmArgs a, int n_tiles
 #pragma unroll
             for (int q = 0; q < 2 * NRB; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (q < NRB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (q % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 // load k after MFMA (k + 1) * 2 NRB / LD - 1
                 if (LD > 0 && ((q + 1) * LD) / (2 * NRB) > (q * LD) / (2 * NRB))
                     __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
