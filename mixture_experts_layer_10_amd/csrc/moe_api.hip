@@ -103,6 +103,23 @@ constexpr size_t kStatusBytes = 256;
 
 int router_chunk(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 64 : 128; }
 
+// The routed GEMMs' plan (bf16 and fp32 layers). With prepacked bf16 weights
+// the 256 x 256 packed tiles pay from about 32 rows per expert, where the
+// LDS-staged canonical tiles need about 256 (plan_gemm): measured on the EP8
+// decode share (32 of 256 experts), per layer, 1024 tokens (32 rows per
+// expert) 0.684 against 0.734 ms, 2048 tokens 0.770 against 0.820 ms, 4096
+// tokens 1.085 against 1.409 ms. The packed down GEMM gains most (2048
+// tokens: 0.245 against 0.284 ms, the shared expert's down beside it 0.197
+// against 0.270).
+GemmPlan routed_plan(const moe_config* c, Epi epi, int64_t P, int El, int64_t per_expert, int N, bool packed) {
+    GemmPlan p = plan_gemm(gemm_elem(c), epi, P, El, per_expert, N);
+    if (!p.big && packed && c->dtype == MOE_DTYPE_BF16 && per_expert >= 32) {
+        const GemmPlan b = plan_gemm_big(epi, P, El, N);
+        if ((P / 256) * b.n_tiles >= 512) p = b;
+    }
+    return p;
+}
+
 // Entries of the tile tables of the routed 256 x 256 launches for a batch of
 // T tokens: the gate/up launch's upper-bound grid, then the down launch's,
 // and 0 when the routed GEMMs do not take 256 x 256 tiles. Non-decreasing in
@@ -111,7 +128,8 @@ int64_t big_tile_entries(const moe_config* c, int64_t T) {
     if (c->dtype != MOE_DTYPE_BF16) return 0;
     const int64_t El = c->expert_end - c->expert_begin, P = T * c->top_k;
     const int64_t per_expert = (P + c->n_experts - 1) / c->n_experts;
-    const GemmPlan p1 = plan_gemm(Elem::BF16, Epi::SWIGLU, P, static_cast<int>(El), per_expert, static_cast<int>(c->inter));
+    // sized for a caller with packed weights (the larger of the two plans)
+    const GemmPlan p1 = routed_plan(c, Epi::SWIGLU, P, static_cast<int>(El), per_expert, static_cast<int>(c->inter), true);
     if (!p1.big) return 0;
     return p1.grid + plan_gemm_big(Epi::PLAIN, P, static_cast<int>(El), static_cast<int>(c->hidden)).grid;
 }
@@ -429,14 +447,14 @@ hipError_t do_routed_ffn(const moe_config* c, int64_t T, const void* x, const in
         StageTimer tm(MOE_STAGE_DOWN, s);
         return launch_quantised(c, Epi::PLAIN, g2, p2, s);
     }
-    GemmPlan p1 = plan_gemm(el, Epi::SWIGLU, P, El, per_expert, static_cast<int>(I));
+    GemmPlan p1 = routed_plan(c, Epi::SWIGLU, P, El, per_expert, static_cast<int>(I), wt->packed != nullptr);
     // 256 x 256 tiles read prepacked weights when the caller has them
     const bool pf = p1.big && wt->packed;
     if (pf) {
         p1.big = 2;
         g1.B = g1.B_shared = packed_ptr(wt, packed_layout(c).w13);
     }
-    GemmPlan p2 = plan_gemm(el, Epi::PLAIN, P, El, per_expert, static_cast<int>(H));
+    GemmPlan p2 = routed_plan(c, Epi::PLAIN, P, El, per_expert, static_cast<int>(H), wt->packed != nullptr);
     if (p2.bm != p1.bm || p2.big != p1.big) {    // the down GEMM reuses the gate/up schedule's m-tiles
         if (p1.big) {
             p2 = plan_gemm_big(Epi::PLAIN, P, El, static_cast<int>(H));   // the same 256 x 256 m-tiles

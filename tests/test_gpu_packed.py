@@ -106,3 +106,13 @@ def test_packed_equals_unpacked_bit_for_bit(name):
 @pytest.mark.parametrize("name", list(PACKED_CASES))
 def test_packed_layer_matches_oracle(name):
     check_layer(PACKED_CASES[name](), f"packed_{name}", packed=True)
+
+
+def test_packed_share_at_64_rows_per_expert_matches_oracle():
+    """An expert-parallel share at about 64 rows per expert: with packed
+    weights the routed GEMMs take the 256 x 256 packed tiles from 32 rows per
+    expert on (tiles of 1-3 row blocks), without them the decode tiles, so
+    only the oracle decides here."""
+    w = _small(T=2048, hidden=256, n_experts=128, expert_end=32, top_k=4, n_group=4, topk_group=2, inter=2048,
+               shared_inter=512, score_bias="zero")
+    check_layer(w, "packed_share_64_rows", packed=True)
