@@ -217,13 +217,14 @@ def test_dispatch_error_word(T, E, k, b, e):
 # tiles split along K (8 slices at 32-63 tiles, 4 at 64-127); every logit
 # against the oracle's fp64 ones. 7900 tokens (31 tiles) stay on the decode
 # tiles; 16000 and 20000 end in a partial tile; 160 experts leave columns of
-# the one column tile past the last expert.
-@pytest.mark.parametrize("T,H,E,bias", [(7900, 4096, 256, True), (8000, 4096, 256, True),
-                                        (16000, 4096, 160, False), (20000, 4096, 256, True),
-                                        (16384, 7168, 256, True)])
-def test_router_gemm_large_batch_every_logit(T, H, E, bias):
-    say("router GEMM, large batch", dict(T=T, H=H, E=E, bias=bias))
-    cfg = moe.make_config(H, E, 8, 256, dtype="bf16")
+# the one column tile past the last expert; an fp8 layer's router (bf16 x and
+# router weights) takes the same path.
+@pytest.mark.parametrize("T,H,E,bias,dtype", [(7900, 4096, 256, True, "bf16"), (8000, 4096, 256, True, "bf16"),
+                                              (16000, 4096, 160, False, "bf16"), (20000, 4096, 256, True, "bf16"),
+                                              (16384, 7168, 256, True, "bf16"), (8192, 4096, 256, True, "fp8")])
+def test_router_gemm_large_batch_every_logit(T, H, E, bias, dtype):
+    say("router GEMM, large batch", dict(T=T, H=H, E=E, bias=bias, dtype=dtype))
+    cfg = moe.make_config(H, E, 8, 256, dtype=dtype)
     g = torch.Generator(device="cuda").manual_seed(T + E)
     x = torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
     wr = (torch.randn(E, H, generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16)
