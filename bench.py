@@ -441,7 +441,7 @@ def measure(name, a, peaks=None):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU: --gpus {a.gpus} is not supported by this build "
+        print(f"bench.py runs on one GPU: --gpus {a.gpus} is not supported "
               "(the layer runs one GPU's share of experts; no collectives).", file=sys.stderr)
         sys.exit(2)
     if a.calibrate_copy:
